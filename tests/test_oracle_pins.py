@@ -1,0 +1,447 @@
+"""Pins of the CPU oracle to facts fixed outside the oracle itself.
+
+Each test checks the oracle against a closed form, a library routine, a
+brute-force search, or a fact the pages print -- never against a retyping of
+the oracle's own formula. Runs on the CPU only.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_bits(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e2m1_table_matches_spec_golden():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "e2m1_table.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 16
+    for code, val in rows:
+        c, v = int(code, 16), float(val)
+        d = oracle.decode("e2m1", c)
+        assert d == v and np.signbit(d) == np.signbit(v), (code, d, v)
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    for c in range(256):
+        d = oracle.decode("e4m3", c)
+        if np.isnan(ref[c]):
+            assert np.isnan(d), c
+        else:
+            assert d == ref[c] and np.signbit(d) == np.signbit(ref[c]), (c, d, ref[c])
+    assert oracle.decode("e4m3", 0x7E) == 448.0
+    assert oracle.decode("e4m3", 0x01) == 2.0 ** -9
+
+
+def test_e8m0_decode_closed_form():
+    for c in range(255):
+        assert oracle.decode("e8m0", c) == 2.0 ** (c - 127)
+    assert np.isnan(oracle.decode("e8m0", 255))
+
+
+def test_encode_inverts_decode_every_code():
+    for c in range(16):
+        assert oracle.encode("e2m1", oracle.decode("e2m1", c)) == c
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue  # NaN codes
+        assert oracle.encode("e4m3", oracle.decode("e4m3", c)) == c
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    r = np.random.default_rng(0)
+    vals = np.concatenate([r.standard_normal(4000) * 50, r.standard_normal(2000) * 1e-2,
+                           r.uniform(-448, 448, 2000)]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v, c in zip(vals, ref):
+        assert oracle.encode("e4m3", float(v)) == c, v
+    # saturation (torch gives NaN out of range; the reading saturates)
+    assert oracle.encode("e4m3", 1000.0) == 0x7E
+    assert oracle.encode("e4m3", -1e6) == 0xFE
+
+
+def _e2m1_nearest_even_bruteforce(v):
+    """Nearest E2M1 magnitude by exhaustive search; ties to the even code."""
+    mags = [oracle.decode("e2m1", c) for c in range(8)]
+    a = min(abs(v), 6.0)
+    best = min(range(8), key=lambda c: (abs(mags[c] - a), c & 1))
+    return best | (8 if np.signbit(v) else 0)
+
+
+def test_e2m1_encode_matches_bruteforce():
+    r = np.random.default_rng(1)
+    vals = list(r.uniform(-8, 8, 3000)) + [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 7.0,
+                                          -0.1, -0.0, 0.0, 6.5, 100.0]
+    for v in vals:
+        assert oracle.encode("e2m1", v) == _e2m1_nearest_even_bruteforce(v), v
+    assert oracle.encode("e2m1", 2.5) == 0x4     # tie 2|3 -> 2 (even mantissa)
+    assert oracle.encode("e2m1", 5.0) == 0x6     # tie 4|6 -> 4
+    assert oracle.encode("e2m1", -0.1) == 0x8    # sign kept on zero
+
+
+def test_rne_bf16_f16_match_libraries():
+    r = np.random.default_rng(2)
+    vals = np.concatenate([r.standard_normal(3000), r.standard_normal(1000) * 1e-5,
+                           r.standard_normal(1000) * 1e4]).astype(np.float32)
+    tb = torch.from_numpy(vals).to(torch.bfloat16).float().numpy()
+    th = vals.astype(np.float16).astype(np.float32)
+    for v, b, h in zip(vals, tb, th):
+        assert oracle.round_to(float(v), "bf16") == b
+        assert oracle.round_to(float(v), "f16") == h
+
+
+@pytest.mark.parametrize("fmt,tdt", [("bf16", torch.bfloat16), ("f16", torch.float16)])
+def test_directed_rounding_brackets(fmt, tdt):
+    """RD/RU give the largest representable <= v and smallest >= v."""
+    r = np.random.default_rng(3)
+    vals = np.concatenate([r.standard_normal(2000) * 0.02, r.standard_normal(500)]).astype(np.float32)
+    for v in vals:
+        d = oracle.round_to(float(v), fmt, "down")
+        u = oracle.round_to(float(v), fmt, "up")
+        td = torch.tensor([d], dtype=torch.float64).to(tdt)
+        tu = torch.tensor([u], dtype=torch.float64).to(tdt)
+        assert float(td) == d and float(tu) == u          # representable
+        assert d <= v <= u
+        if d != v:
+            nxt = torch.nextafter(td, torch.tensor([np.inf], dtype=tdt))
+            assert float(nxt) > v and u == float(nxt)
+
+
+# ---------------------------------------------------------------- affine
+
+def _grid_exact(rows, K, g, bits, seed, smin=-6):
+    """w = z + s*q with power-of-two s, integer z, codes 0 and n in every group."""
+    r = np.random.default_rng(seed)
+    n = (1 << bits) - 1
+    G = K // g
+    q = r.integers(0, n + 1, size=(rows, K))
+    q[:, ::g] = 0
+    q[:, 1::g] = n
+    s = 2.0 ** r.integers(smin, 1, size=(rows, G))
+    z = r.integers(-8, 8, size=(rows, G)).astype(np.float64)
+    w = z.repeat(g, 1) + s.repeat(g, 1) * q
+    return w.astype(np.float32), q, s, z
+
+
+def _unpack(wq, bits, K):
+    per = 32 // bits
+    k = np.arange(K)
+    return (wq[..., k // per] >> ((k % per) * bits).astype(np.uint32)) & ((1 << bits) - 1)
+
+
+@pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 128), (4, 32), (8, 64), (2, 128)])
+def test_affine_grid_exact_closed_form(bits, g):
+    w, q, s, z = _grid_exact(6, 256, g, bits, seed=bits * 100 + g)
+    wq, sc, bi = oracle.quantize(w, "f32", g, bits)
+    assert wq.shape == (6, 256 * bits // 32)
+    assert np.array_equal(_unpack(wq, bits, 256), q)
+    assert np.array_equal(sc.astype(np.float64), s)
+    assert np.array_equal(bi.astype(np.float64), z)
+    dq = oracle.dequantize(wq, sc, bi, g, bits, scale_dtype="f32")
+    assert np.array_equal(dq, w)
+
+
+def test_affine_grid_exact_bf16_storage():
+    w, q, s, z = _grid_exact(4, 128, 64, 4, seed=7, smin=-2)
+    wb = bf16_bits(w)
+    assert np.array_equal(bf16_to_f32(wb), w)  # grid values are bf16-exact
+    wq, sc, bi = oracle.quantize(wb, "bf16", 64, 4)
+    assert np.array_equal(_unpack(wq, 4, 128), q)
+    assert np.array_equal(bf16_to_f32(sc).astype(np.float64), s)
+    assert np.array_equal(bf16_to_f32(bi).astype(np.float64), z)
+
+
+def test_packing_word_layout():
+    # codes 0..7 then 15 in the first group: the first word is 0x76543210
+    w = np.zeros((1, 64), np.float32)
+    w[0, :8] = np.arange(8)
+    w[0, 8] = 15
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    assert sc[0, 0] == 1.0 and bi[0, 0] == 0.0
+    assert wq[0, 0] == 0x76543210 and wq[0, 1] == 0xF
+    # 8-bit: a group holding 0..255 maps to itself, little-endian bytes
+    w8 = np.tile(np.arange(128, dtype=np.float32), (1, 1))
+    w8[0, 1] = 255
+    wq8, sc8, bi8 = oracle.quantize(w8, "f32", 128, 8)
+    assert sc8[0, 0] == 1.0 and bi8[0, 0] == 0.0
+    assert np.array_equal(wq8.view(np.uint8)[0], w8[0].astype(np.uint8))
+    # 2-bit: codes 0,1,2,3,3,2,1,0,... -> bits 2k..2k+1
+    w2 = np.array([[0, 1, 2, 3, 3, 2, 1, 0] * 4], np.float32)
+    wq2, _, _ = oracle.quantize(w2, "f32", 32, 2)
+    expect = sum(c << (2 * i) for i, c in enumerate([0, 1, 2, 3, 3, 2, 1, 0, 0, 1, 2, 3, 3, 2, 1, 0]))
+    assert wq2[0, 0] == expect
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rs_quantize_dequantize_roundtrip(bits):
+    """mlx-rs test_quantize_dequantize: rows of 0..511, group 128."""
+    x = np.tile(np.arange(512, dtype=np.float32), (128, 1))
+    wq, sc, bi = oracle.quantize(x, "f32", 128, bits)
+    assert wq.shape == (128, 512 // (32 // bits))
+    assert sc.shape == (128, 4) and bi.shape == (128, 4)
+    xh = oracle.dequantize(wq, sc, bi, 128, bits, scale_dtype="f32")
+    assert np.abs(x - xh).max() <= 127.0 / (1 << bits)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 64), (4, 128)])
+def test_affine_error_bound_half_scale(dtype, bits, g):
+    t, wbits = synth.normal((16, 512), 0.02, 99, bits * 1000 + g, dtype)
+    wf = t.float().numpy()
+    wq, sc, bi = oracle.quantize(wbits, dtype, g, bits)
+    s = (sc.astype(np.float32) if dtype == "f32" else
+         torch.from_numpy(sc.view(np.int16)).view(torch.bfloat16 if dtype == "bf16" else torch.float16).float().numpy())
+    dq = oracle.dequantize(wq, sc, bi, g, bits, scale_dtype=dtype)
+    err = np.abs(wf - dq).reshape(16, -1, g)
+    half = s[..., None] / 2
+    # |w - dq| <= s/2 up to the single fp32 rounding of dq
+    assert np.all(err <= half * (1 + 2 ** -20) + np.abs(dq).reshape(16, -1, g) * 2 ** -24)
+
+
+def test_constant_group_is_exact():
+    w = np.full((2, 64), 0.3, np.float32)
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    assert sc[0, 0] == 0 and np.all(wq == 0)
+    assert np.array_equal(oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32"), w)
+
+
+def test_dequant_output_dtypes_match_library_rounding():
+    t, wbits = synth.normal((8, 256), 1.0, 5, 0, "f32")
+    wq, sc, bi = oracle.quantize(wbits, "f32", 64, 4)
+    d32 = oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32", out_dtype="f32")
+    db = oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32", out_dtype="bf16")
+    dh = oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32", out_dtype="f16")
+    assert np.array_equal(db, bf16_bits(d32))
+    assert np.array_equal(dh, d32.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------- microscaled
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8", "nvfp4"])
+def test_micro_grid_exact_closed_form(mode):
+    """Elements = code values x a chosen scale, with the group maximum present:
+    quantize must return those codes and that scale byte exactly."""
+    g, bits = oracle.MODE_PAIRING[mode]
+    r = np.random.default_rng(11)
+    rows, K = 5, 4 * g
+    G = K // g
+    fmt = "e4m3" if mode == "mxfp8" else "e2m1"
+    ncode = 1 << bits
+    valid = [c for c in range(ncode) if not (fmt == "e4m3" and (c & 0x7F) == 0x7F)]
+    codes = r.choice(valid, size=(rows, K))
+    maxcode = 0x7E if fmt == "e4m3" else 0x7
+    codes[:, ::g] = maxcode                      # amax present in every group
+    vals = np.vectorize(lambda c: oracle.decode(fmt, int(c)))(codes)
+    if mode == "nvfp4":
+        sbytes = r.integers(0x20, 0x60, size=(rows, G))   # normal e4m3 scales
+        scale = np.vectorize(lambda c: oracle.decode("e4m3", int(c)))(sbytes)
+    else:
+        e = r.integers(-20, 20, size=(rows, G))
+        sbytes = e + 127
+        scale = 2.0 ** e
+    w = (vals * scale.repeat(g, 1)).astype(np.float32)
+    assert np.array_equal(w.astype(np.float64), vals * scale.repeat(g, 1))
+    wq, sc, bi = oracle.quantize(w, "f32", g, bits, mode)
+    assert bi is None and sc.dtype == np.uint8
+    assert np.array_equal(sc, sbytes.astype(np.uint8))
+    got = _unpack(wq, bits, K)
+    # -0 and +0 both decode to 0; compare values, and codes where nonzero
+    nz = vals != 0
+    assert np.array_equal(got[nz], codes[nz])
+    dq = oracle.dequantize(wq, sc, None, g, bits, mode)
+    assert np.array_equal(dq, w)
+
+
+def test_mx_shared_exponent_rule():
+    # amax in [4, 8) -> floor(log2 amax) = 2 -> e = 0 for E2M1 (emax 2)
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0], w[0, 1], w[0, 2] = 7.0, 2.5, -0.1
+    wq, sc, _ = oracle.quantize(w, "f32", 32, 4, "mxfp4")
+    assert sc[0, 0] == 127
+    c = _unpack(wq, 4, 32)[0]
+    assert c[0] == 0x7 and c[1] == 0x4 and c[2] == 0x8   # saturate 7->6, tie 2.5->2, -0
+    # all zeros -> byte 0, codes 0
+    wz = np.zeros((1, 32), np.float32)
+    wq, sc, _ = oracle.quantize(wz, "f32", 32, 8, "mxfp8")
+    assert sc[0, 0] == 0 and np.all(wq == 0)
+    # nvfp4: scale = e4m3(amax/6)
+    w = np.zeros((1, 16), np.float32)
+    w[0, 0] = 12.0
+    wq, sc, _ = oracle.quantize(w, "f32", 16, 4, "nvfp4")
+    assert oracle.decode("e4m3", sc[0, 0]) == 2.0 and _unpack(wq, 4, 16)[0, 0] == 0x7
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8", "nvfp4"])
+def test_micro_error_bound(mode):
+    g, bits = oracle.MODE_PAIRING[mode]
+    t, wbits = synth.normal((8, 512), 0.02, 3, 0, "bf16")
+    wf = t.float().numpy()
+    wq, sc, _ = oracle.quantize(wbits, "bf16", g, bits, mode)
+    dq = oracle.dequantize(wq, sc, None, g, bits, mode)
+    fmt = "e4m3" if mode == "mxfp8" else "e2m1"
+    sfmt = "e4m3" if mode == "nvfp4" else "e8m0"
+    scale = np.vectorize(lambda c: oracle.decode(sfmt, int(c)))(sc).repeat(g, 1)
+    v = np.abs(wf) / scale
+    # half the element-grid spacing at |v| (mantissa bits 1 / 3), plus saturation
+    p = 2 if fmt == "e2m1" else 4
+    emin = 0 if fmt == "e2m1" else -6
+    E = np.maximum(np.floor(np.log2(np.maximum(v, 1e-30))), emin)
+    half = 2.0 ** (E - p + 1) / 2 * scale
+    maxv = 6.0 if fmt == "e2m1" else 448.0
+    sat = np.maximum(np.abs(wf) - maxv * scale, 0)
+    assert np.all(np.abs(wf - dq) <= half + sat + 1e-30)
+
+
+def test_mode_pairing_rejected():
+    w = np.zeros((2, 64), np.float32)
+    for mode, (g, b) in oracle.MODE_PAIRING.items():
+        oracle.quantize(w, "f32", g, b, mode)  # accepted
+        for gg, bb in [(64, b), (g, 2), (128, 8)]:
+            if (gg, bb) != (g, b):
+                with pytest.raises(oracle.OracleError):
+                    oracle.quantize(w, "f32", gg, bb, mode)
+    for bad in [(64, 3), (64, 6), (16, 4), (48, 4)]:
+        with pytest.raises(oracle.OracleError):
+            oracle.quantize(w, "f32", bad[0], bad[1], "affine")
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize(np.zeros((2, 96), np.float32), "f32", 64, 4)   # 64 does not divide 96
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize(w, "f32", 64, 4, "int4")
+
+
+# ---------------------------------------------------------------- matmul
+
+@pytest.mark.parametrize("transpose", [True, False])
+@pytest.mark.parametrize("bits,g", [(4, 64), (2, 32), (8, 128)])
+def test_qmm_grid_exact_equals_integer_matmul(transpose, bits, g):
+    N, K, M = 128, 256, 5
+    rows, cols = (N, K) if transpose else (K, N)
+    w, q, s, z = _grid_exact(rows, cols, g, bits, seed=31 + bits)
+    x = np.random.default_rng(4).integers(-3, 4, size=(M, K)).astype(np.float32)
+    wq, sc, bi = oracle.quantize(w, "f32", g, bits)
+    y = oracle.quantized_matmul(x, "f32", wq, sc, bi, transpose, g, bits)
+    W = w.astype(np.float64)
+    ref = x.astype(np.float64) @ (W.T if transpose else W)
+    assert np.array_equal(y, ref)
+    assert y.shape == (M, N)
+
+
+def test_qmm_bruteforce_tiny():
+    """Every output element against an explicit fp64 triple loop."""
+    t, wb = synth.normal((8, 64), 0.5, 21, 0, "bf16")
+    tx, xb = synth.normal((3, 64), 1.0, 21, 1, "bf16")
+    wq, sc, bi = oracle.quantize(wb, "bf16", 32, 4)
+    y = oracle.quantized_matmul(xb, "bf16", wq, sc, bi, True, 32, 4)
+    q = _unpack(wq, 4, 64).astype(np.float64)
+    s = bf16_to_f32(sc).astype(np.float64)
+    z = bf16_to_f32(bi).astype(np.float64)
+    xf = bf16_to_f32(xb).astype(np.float64)
+    for m in range(3):
+        for n in range(8):
+            acc, bound = 0.0, 0.0
+            for k in range(64):
+                wv = s[n, k // 32] * q[n, k] + z[n, k // 32]      # exact in fp64
+                acc += xf[m, k] * wv
+                bound += abs(xf[m, k]) * abs(wv) * 2.0 ** -24       # one fp32 rounding of wv
+            assert abs(y[m, n] - acc) <= bound + 1e-12
+
+
+def test_rs_quantized_matmul_transpose_false():
+    """mlx-rs test_quantized_matmul: transpose=false, max diff < 1e-3."""
+    m, n, k = 32, 128, 128
+    sc_ = 1.0 / np.sqrt(k)
+    tx, x = synth.normal((m, k), sc_, 1001, 1, "f32")
+    tw, w = synth.normal((k, n), sc_, 1001, 0, "f32")
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    w_hat = oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32")
+    y = oracle.quantized_matmul(x, "f32", wq, sc, bi, False, 64, 4)
+    y_hat = x.astype(np.float32) @ w_hat
+    assert y.shape == y_hat.shape == (m, n)
+    assert np.abs(y - y_hat).max() < 1e-3
+
+
+def test_page_example_shapes():
+    # "Emily.QuantizedWeight" from_dense / to_dense examples
+    t, w = synth.iota((4, 64))
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    assert wq.shape == (4, 8)
+    assert oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32").shape == (4, 64)
+    # "Emily.Quantization.Layers" quantized_dense example: {2,128} . {4,128} -> {2,4}
+    t, w = synth.iota((4, 128))
+    t, x = synth.iota((2, 128))
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    y = oracle.quantized_matmul(x, "f32", wq, sc, bi, True, 64, 4)
+    assert y.shape == (2, 4)
+    # each W group is 64 consecutive integers: |y - x.W^T| <= sum|x| * scale/2
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.all(np.abs(y - exact) <= np.abs(x).sum(1, keepdims=True) * (63 / 15) / 2 * 1.0001)
+    # "EMLX.Quantization" basic usage: {1,8,4096} . {512,4096} -> {1,8,512}
+    t, w = synth.iota((512, 4096))
+    t, x = synth.iota((1, 8, 4096))
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    y = oracle.quantized_matmul(x, "f32", wq, sc, bi, True, 64, 4)
+    assert y.shape == (1, 8, 512)
+
+
+# ---------------------------------------------------------------- gather
+
+def test_gather_grid_exact_and_rs_cases():
+    E, N, K, M = 3, 64, 64, 32
+    ws = [_grid_exact(N, K, 64, 4, seed=50 + e)[0] for e in range(E)]
+    w = np.stack(ws)
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    r = np.random.default_rng(8)
+    for B, lhs in [(1, [0]), (5, [0, 2])]:
+        x = r.integers(-2, 3, size=(B, M, K)).astype(np.float32)
+        rhs = [2, 1]
+        lhs_b = np.broadcast_to(np.array(lhs), (2,))
+        y = oracle.gather_qmm(x, "f32", wq, sc, bi, rhs, lhs_b, True, 64, 4)
+        for i in range(2):
+            ref = x[lhs_b[i]].astype(np.float64) @ w[rhs[i]].astype(np.float64).T
+            assert np.array_equal(y[i], ref)
+
+
+def test_rs_gather_qmm_cases():
+    """mlx-rs test_gather_qmm, both index cases, against gather_mm on w_hat."""
+    m, n, k = 32, 64, 64
+    tw, w = synth.normal((3, n, k), 1.0, 2002, 0, "f32")
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    w_hat = oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32")
+    for B, lhs in [(1, [0, 0]), (5, [0, 2])]:
+        tx, x = synth.normal((B, m, k), 1.0, 2002, 1 + B, "f32")
+        rhs = [2, 1]
+        c1 = np.stack([x[lhs[i]] @ w_hat[rhs[i]].T for i in range(2)])
+        c2 = oracle.gather_qmm(x, "f32", wq, sc, bi, rhs, lhs, True, 64, 4)
+        assert np.allclose(c1, c2, rtol=1e-4, atol=1e-4)
+
+
+def test_gather_permutation_and_identity():
+    E, N, K, M = 4, 32, 128, 2
+    tw, w = synth.normal((E, N, K), 0.02, 7, 0, "bf16")
+    tx, x = synth.normal((6, M, K), 1.0, 7, 1, "bf16")
+    wq, sc, bi = oracle.quantize(w, "bf16", 64, 4)
+    rhs = np.array([3, 0, 1, 3, 2, 0])
+    y = oracle.gather_qmm(x, "bf16", wq, sc, bi, rhs, None, True, 64, 4)
+    perm = np.array([5, 2, 0, 4, 1, 3])
+    yp = oracle.gather_qmm(x, "bf16", wq, sc, bi, rhs[perm], perm, True, 64, 4)
+    assert np.array_equal(yp, y[perm])
+    # constant rhs = a plain quantized matmul on that expert
+    y1 = oracle.gather_qmm(x, "bf16", wq, sc, bi, np.full(6, 2), None, True, 64, 4)
+    ref = oracle.quantized_matmul(x.reshape(-1, K), "bf16", wq[2], sc[2], bi[2], True, 64, 4)
+    assert np.array_equal(y1.reshape(-1, N), ref)
