@@ -1,0 +1,168 @@
+/*
+ * qlin.h -- C ABI of the MI355X (gfx950) group-wise quantization library.
+ *
+ * The library implements the operations described on these pages:
+ *   "EMLX.Quantization" (emlx 0.4.2): quantize, dequantize,
+ *       quantized_matmul, gather_quantized_matmul sections;
+ *   "Emily.QuantizedWeight" (emily 0.7.2): Layout section and the
+ *       Microscaled modes table;
+ *   "Emily.Quantization.Layers" (emily 1.0.0): quantized_dense (the two
+ *       weight layouts selected by `transpose`);
+ *   mlx-rs "ops/quantization.rs" source: the quantize, quantized_matmul,
+ *       dequantize and gather_qmm functions and their argument lists.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor is dense and row-major; every data pointer is a DEVICE
+ *   pointer (memory from hipMalloc or a PyTorch CUDA/HIP tensor) on the
+ *   current HIP device. Sizes are element counts.
+ * - Ownership: the caller allocates and frees every buffer (inputs, outputs,
+ *   workspace). The library never allocates, frees or keeps a pointer after
+ *   the call returns.
+ * - Asynchrony: all work is enqueued on `stream` (a hipStream_t; NULL means
+ *   the default stream). The library never synchronises the host; buffers
+ *   must stay alive until the stream has run the work.
+ * - Errors: every argument is checked on the host before anything is
+ *   launched; a rejected call launches nothing and leaves outputs untouched.
+ *   The return value is a qlin_status; qlin_last_error() gives a message for
+ *   the calling thread's last failure.
+ * - Packing ("Emily.QuantizedWeight", Layout): codes of `bits` bits are
+ *   packed 32/bits per uint32 word along the last axis, the element with the
+ *   lowest index in the least significant bits.
+ * - Modes ("Emily.QuantizedWeight", Microscaled modes table):
+ *     "affine": bits in {2,4,8}, group_size in {32,64,128}; per group one
+ *               scale and one bias, stored in the weight's float dtype;
+ *     "mxfp4":  group 32, 4-bit E2M1 codes, one E8M0 scale byte per group;
+ *     "mxfp8":  group 32, 8-bit E4M3 codes, one E8M0 scale byte per group;
+ *     "nvfp4":  group 16, 4-bit E2M1 codes, one E4M3 scale byte per group.
+ *   Microscaled modes have no biases (pass NULL). A (mode, group_size, bits)
+ *   mismatch is QLIN_ERR_INVALID_ARGUMENT.
+ * - Thread safety: no global mutable state besides the per-thread error
+ *   text; concurrent calls on different streams are independent.
+ */
+#ifndef QLIN_H
+#define QLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qlin_dtype {
+    QLIN_F32 = 0,
+    QLIN_F16 = 1,
+    QLIN_BF16 = 2,
+    QLIN_U8 = 3
+} qlin_dtype;
+
+typedef enum qlin_status {
+    QLIN_OK = 0,
+    QLIN_ERR_INVALID_ARGUMENT = 1, /* bad shape, dtype, mode, pairing, pointer */
+    QLIN_ERR_UNSUPPORTED = 2,      /* valid combination this build does not run */
+    QLIN_ERR_DEVICE = 3            /* a HIP launch or runtime call failed */
+} qlin_status;
+
+/*
+ * qlin_quantize -- group-wise quantization of w [rows, cols] along cols.
+ * ("EMLX.Quantization" quantize: rank >= 2, quantized along the last axis,
+ * leading axes flattened into `rows`; mlx-rs quantize returns (wq, scales,
+ * biases).)
+ *   w        [rows, cols] of w_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16).
+ *   wq       out, uint32 [rows, cols*bits/32].
+ *   scales   out, [rows, cols/group_size]: w_dtype for "affine", uint8 bytes
+ *            (E8M0 for mxfp4/mxfp8, E4M3 for nvfp4) otherwise.
+ *   biases   out, like scales for "affine"; must be NULL otherwise.
+ * Affine rule (the pages give only w ~ scale*q + bias): bias = group minimum
+ * rounded down into w_dtype, scale = (max - bias)/(2^bits - 1) computed in
+ * fp32 and rounded up into w_dtype, q = nearest-even of (w - bias)/scale in
+ * fp32, clamped to [0, 2^bits-1]; a constant group has scale 0, codes 0.
+ * Microscaled rule: OCP MX shared exponent floor(log2 amax) - emax_elem for
+ * mxfp4/mxfp8; E4M3(amax/6) for nvfp4; elements nearest-even, saturating.
+ * Requires cols % group_size == 0 and rows >= 1.
+ */
+qlin_status qlin_quantize(const void* w, qlin_dtype w_dtype, int64_t rows, int64_t cols,
+                          int group_size, int bits, const char* mode, uint32_t* wq,
+                          void* scales, void* biases, void* stream);
+
+/*
+ * qlin_dequantize -- dense weight from its quantized form
+ * ("EMLX.Quantization" dequantize: the output has the logical shape; mlx-rs
+ * dequantize takes an optional output dtype).
+ *   wq [rows, cols*bits/32], scales/biases [rows, cols/group_size] as
+ *   produced by qlin_quantize; scale_dtype is the float dtype of scales and
+ *   biases for "affine" and must be QLIN_U8 otherwise.
+ *   out [rows, cols] in out_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16).
+ * Affine: out = round(fmaf(scale, q, bias)) -- one fp32 rounding, then
+ * nearest-even into out_dtype. Microscaled: decode(q) * decode(scale byte).
+ */
+qlin_status qlin_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                            qlin_dtype scale_dtype, int64_t rows, int64_t cols, int group_size,
+                            int bits, const char* mode, void* out, qlin_dtype out_dtype,
+                            void* stream);
+
+/*
+ * qlin_quantized_matmul -- fused y = x . W^T (transpose != 0) or y = x . W
+ * (transpose == 0) on the quantized weight, without writing a dense W
+ * ("EMLX.Quantization" quantized_matmul; "Emily.Quantization.Layers"
+ * quantized_dense: transpose true is the [out, in] layout, false the
+ * [in, out] layout).
+ *   x   [M, K] of x_dtype (QLIN_F32, QLIN_F16 or QLIN_BF16); leading batch
+ *       dims flattened into M; M == 0 is a no-op.
+ *   wq  transpose: [N, K*bits/32], groups along K;
+ *       else:      [K, N*bits/32], groups along N.
+ *   scales/biases  transpose: [N, K/group_size]; else [K, N/group_size].
+ *   y   out, [M, N] of x_dtype. For "affine" the output follows the scales
+ *       dtype, so scale_dtype must equal x_dtype; microscaled output
+ *       follows x.
+ * Products accumulate in fp32.
+ */
+qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                  const uint32_t* wq, const void* scales, const void* biases,
+                                  qlin_dtype scale_dtype, int64_t N, int transpose,
+                                  int group_size, int bits, const char* mode, void* y,
+                                  void* stream);
+
+/*
+ * qlin_gather_qmm_workspace_bytes -- device workspace qlin_gather_qmm needs
+ * for R index rows over E experts (bucket offsets, counts and the row
+ * permutation). Always > 0.
+ */
+size_t qlin_gather_qmm_workspace_bytes(int64_t R, int64_t E);
+
+/*
+ * qlin_gather_qmm -- mixture-of-experts quantized matmul
+ * ("EMLX.Quantization" gather_quantized_matmul; mlx-rs gather_qmm):
+ *   y[r] = x[lhs[r]] . W[rhs[r]]^T   (transpose != 0), or with W[rhs[r]]
+ * for r in [0, R). The expert gather happens inside the op: expert weights
+ * are read in place and never copied per row.
+ *   x    [B, M, K] of x_dtype.
+ *   wq   experts stacked on the leading axis: [E, N, K*bits/32] (transpose)
+ *        or [E, K, N*bits/32]; scales/biases [E, N, K/g] or [E, K, N/g].
+ *   lhs_indices  uint32 [R] in [0, B), or NULL meaning lhs[r] = r (then
+ *        B must equal R). Reorders / selects activation rows.
+ *   rhs_indices  uint32 [R] in [0, E): the expert of each row.
+ *   sorted_indices  nonzero promises rhs is non-decreasing, so the library
+ *        skips its own bucketing; results never depend on it.
+ *   workspace  device buffer of at least
+ *        qlin_gather_qmm_workspace_bytes(R, E) bytes, owned by the caller.
+ *   y    out, [R, M, N] of x_dtype (same dtype rule as quantized_matmul).
+ * Index values are a precondition (not checked on the device).
+ */
+qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_t M, int64_t K,
+                            const uint32_t* wq, const void* scales, const void* biases,
+                            qlin_dtype scale_dtype, int64_t E, int64_t N,
+                            const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t R,
+                            int transpose, int group_size, int bits, const char* mode,
+                            int sorted_indices, void* workspace, size_t workspace_bytes, void* y,
+                            void* stream);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* qlin_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLIN_H */

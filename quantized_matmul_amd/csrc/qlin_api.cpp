@@ -1,0 +1,257 @@
+// qlin_api.cpp -- the C ABI of libqlin: argument validation and kernel
+// dispatch. Every argument is checked on the host before anything is
+// launched, so a rejected call has no device side effects (the pages ask for
+// a clear error before the backend is touched: "Emily.QuantizedWeight",
+// Microscaled modes section).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/qlin.h"
+#include "qlin_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qlin_status fail(qlin_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+qlin_status ok() {
+    g_last_error.clear();
+    return QLIN_OK;
+}
+
+qlin_status device_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(QLIN_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_float_dtype(int d) { return d == QLIN_F32 || d == QLIN_F16 || d == QLIN_BF16; }
+
+// Parse the mode string and check (group_size, bits) against it and against
+// the quantized axis length.
+qlin_status check_mode(const char* mode, int group_size, int bits, int64_t qaxis, int* mode_out) {
+    if (!mode) return fail(QLIN_ERR_INVALID_ARGUMENT, "mode is NULL");
+    int m;
+    if (!strcmp(mode, "affine")) m = qlin::AFFINE;
+    else if (!strcmp(mode, "mxfp4")) m = qlin::MXFP4;
+    else if (!strcmp(mode, "mxfp8")) m = qlin::MXFP8;
+    else if (!strcmp(mode, "nvfp4")) m = qlin::NVFP4;
+    else return fail(QLIN_ERR_INVALID_ARGUMENT, "unknown mode \"%s\" (affine, mxfp4, mxfp8, nvfp4)", mode);
+    if (m == qlin::AFFINE) {
+        if (bits != 2 && bits != 4 && bits != 8)
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "affine bits must be 2, 4 or 8 (got %d)", bits);
+        if (group_size != 32 && group_size != 64 && group_size != 128)
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "affine group_size must be 32, 64 or 128 (got %d)",
+                        group_size);
+    } else {
+        const int g = (m == qlin::NVFP4) ? 16 : 32, b = (m == qlin::MXFP8) ? 8 : 4;
+        if (group_size != g || bits != b)
+            return fail(QLIN_ERR_INVALID_ARGUMENT,
+                        "mode %s requires group_size %d and bits %d (got %d and %d)", mode, g, b,
+                        group_size, bits);
+    }
+    if (qaxis <= 0 || qaxis % group_size != 0)
+        return fail(QLIN_ERR_INVALID_ARGUMENT,
+                    "quantized axis length %lld must be a positive multiple of group_size %d",
+                    (long long)qaxis, group_size);
+    *mode_out = m;
+    return QLIN_OK;
+}
+
+qlin_status check_scale_dtype(int mode, int scale_dtype, const void* biases) {
+    if (mode == qlin::AFFINE) {
+        if (!is_float_dtype(scale_dtype))
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "affine scales must be f32, f16 or bf16");
+        if (!biases) return fail(QLIN_ERR_INVALID_ARGUMENT, "affine mode needs biases");
+    } else {
+        if (scale_dtype != QLIN_U8)
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "microscaled scales are uint8 bytes");
+        if (biases) return fail(QLIN_ERR_INVALID_ARGUMENT, "microscaled modes take no biases");
+    }
+    return QLIN_OK;
+}
+
+// Kernel path override for tests of each code path ("generic", "decode",
+// "tiled"); unset means automatic choice.
+int forced_path() {
+    const char* e = getenv("QLIN_FORCE_PATH");
+    if (!e || !*e) return 0;
+    if (!strcmp(e, "generic")) return 1;
+    if (!strcmp(e, "decode")) return 2;
+    if (!strcmp(e, "tiled")) return 3;
+    return 0;
+}
+
+qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t* offsets,
+                    hipStream_t st) {
+    const int force = forced_path();
+    if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_decode_supports(a))
+        return device_status(qlin::launch_qmm_decode(a, st), "quantized_matmul (decode kernel)");
+    if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
+    if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
+        return device_status(qlin::launch_qmm_tiled(a, perm, offsets, st),
+                             "quantized_matmul (tiled kernel)");
+    if (force == 3) return fail(QLIN_ERR_UNSUPPORTED, "tiled kernel does not take this shape");
+    return device_status(qlin::launch_qmm_generic(a, st), "quantized_matmul (generic kernel)");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlin_last_error(void) { return g_last_error.c_str(); }
+
+qlin_status qlin_quantize(const void* w, qlin_dtype w_dtype, int64_t rows, int64_t cols,
+                          int group_size, int bits, const char* mode, uint32_t* wq, void* scales,
+                          void* biases, void* stream) {
+    int m;
+    qlin_status st = check_mode(mode, group_size, bits, cols, &m);
+    if (st) return st;
+    if (!is_float_dtype(w_dtype)) return fail(QLIN_ERR_INVALID_ARGUMENT, "w must be f32, f16 or bf16");
+    if (rows < 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+    if (m == qlin::AFFINE && !biases) return fail(QLIN_ERR_INVALID_ARGUMENT, "affine mode needs biases");
+    if (m != qlin::AFFINE && biases)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "microscaled modes take no biases (pass NULL)");
+    if (rows == 0) return ok();
+    if (!w || !wq || !scales) return fail(QLIN_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    return device_status(qlin::launch_quantize(w, w_dtype, rows, cols, group_size, bits, m, wq,
+                                               scales, biases, (hipStream_t)stream),
+                         "quantize");
+}
+
+qlin_status qlin_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                            qlin_dtype scale_dtype, int64_t rows, int64_t cols, int group_size,
+                            int bits, const char* mode, void* out, qlin_dtype out_dtype,
+                            void* stream) {
+    int m;
+    qlin_status st = check_mode(mode, group_size, bits, cols, &m);
+    if (st) return st;
+    if ((st = check_scale_dtype(m, scale_dtype, biases))) return st;
+    if (!is_float_dtype(out_dtype)) return fail(QLIN_ERR_INVALID_ARGUMENT, "out must be f32, f16 or bf16");
+    if (rows < 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+    if (rows == 0) return ok();
+    if (!wq || !scales || !out) return fail(QLIN_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    return device_status(qlin::launch_dequantize(wq, scales, biases, scale_dtype, rows, cols,
+                                                 group_size, bits, m, out, out_dtype,
+                                                 (hipStream_t)stream),
+                         "dequantize");
+}
+
+qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                  const uint32_t* wq, const void* scales, const void* biases,
+                                  qlin_dtype scale_dtype, int64_t N, int transpose, int group_size,
+                                  int bits, const char* mode, void* y, void* stream) {
+    int m;
+    if (N <= 0 || K <= 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "N and K must be positive");
+    qlin_status st = check_mode(mode, group_size, bits, transpose ? K : N, &m);
+    if (st) return st;
+    if ((st = check_scale_dtype(m, scale_dtype, biases))) return st;
+    if (!is_float_dtype(x_dtype)) return fail(QLIN_ERR_INVALID_ARGUMENT, "x must be f32, f16 or bf16");
+    if (m == qlin::AFFINE && scale_dtype != x_dtype)
+        return fail(QLIN_ERR_INVALID_ARGUMENT,
+                    "affine output follows the scales dtype: x and scales must share a dtype");
+    if (M < 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "M must be >= 0");
+    if (M == 0) return ok();
+    if (!x || !wq || !scales || !y) return fail(QLIN_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31))
+        return fail(QLIN_ERR_UNSUPPORTED, "dimensions above 2^31 are not supported");
+    qlin::QmmArgs a{};
+    a.x = x;
+    a.wq = wq;
+    a.scales = scales;
+    a.biases = biases;
+    a.y = y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.x_dtype = x_dtype;
+    a.scale_dtype = scale_dtype;
+    a.transpose = transpose ? 1 : 0;
+    a.group_size = group_size;
+    a.bits = bits;
+    a.mode = m;
+    return run_qmm(a, nullptr, nullptr, (hipStream_t)stream);
+}
+
+size_t qlin_gather_qmm_workspace_bytes(int64_t R, int64_t E) {
+    if (R < 0) R = 0;
+    if (E < 0) E = 0;
+    return qlin::bucket_workspace_bytes(R, E);
+}
+
+qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_t M, int64_t K,
+                            const uint32_t* wq, const void* scales, const void* biases,
+                            qlin_dtype scale_dtype, int64_t E, int64_t N,
+                            const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t R,
+                            int transpose, int group_size, int bits, const char* mode,
+                            int sorted_indices, void* workspace, size_t workspace_bytes, void* y,
+                            void* stream) {
+    int m;
+    if (N <= 0 || K <= 0 || E <= 0)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "N, K and E must be positive");
+    qlin_status st = check_mode(mode, group_size, bits, transpose ? K : N, &m);
+    if (st) return st;
+    if ((st = check_scale_dtype(m, scale_dtype, biases))) return st;
+    if (!is_float_dtype(x_dtype)) return fail(QLIN_ERR_INVALID_ARGUMENT, "x must be f32, f16 or bf16");
+    if (m == qlin::AFFINE && scale_dtype != x_dtype)
+        return fail(QLIN_ERR_INVALID_ARGUMENT,
+                    "affine output follows the scales dtype: x and scales must share a dtype");
+    if (R < 0 || M < 0 || B < 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "negative size");
+    if (!lhs_indices && B != R)
+        return fail(QLIN_ERR_INVALID_ARGUMENT,
+                    "without lhs_indices, x must have one batch entry per index row (B == R)");
+    if (R == 0 || M == 0) return ok();
+    if (B == 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "x has no batch entries");
+    if (!x || !wq || !scales || !y || !rhs_indices)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    const size_t need = qlin::bucket_workspace_bytes(R, E);
+    if (!workspace || workspace_bytes < need)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace_bytes);
+    if (R * M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31) || E > (1LL << 31))
+        return fail(QLIN_ERR_UNSUPPORTED, "dimensions above 2^31 are not supported");
+    qlin::QmmArgs a{};
+    a.x = x;
+    a.wq = wq;
+    a.scales = scales;
+    a.biases = biases;
+    a.y = y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.x_dtype = x_dtype;
+    a.scale_dtype = scale_dtype;
+    a.transpose = transpose ? 1 : 0;
+    a.group_size = group_size;
+    a.bits = bits;
+    a.mode = m;
+    a.batch_x = B;
+    a.R = R;
+    a.E = E;
+    a.lhs = lhs_indices;
+    a.rhs = rhs_indices;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t *perm = nullptr, *offsets = nullptr;
+    if (qlin::qmm_tiled_supports(a) && forced_path() != 1) {
+        hipError_t e = qlin::launch_bucket(rhs_indices, R, E, M, sorted_indices, workspace, &perm,
+                                           &offsets, s);
+        if (e != hipSuccess) return device_status(e, "gather_qmm (expert bucketing)");
+    }
+    return run_qmm(a, perm, offsets, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// qlin_common.h -- device helpers and internal launcher declarations shared by
+// the HIP translation units of libqlin (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qlin.h"
+
+namespace qlin {
+
+enum Mode : int { AFFINE = 0, MXFP4 = 1, MXFP8 = 2, NVFP4 = 3 };
+
+// ---------------------------------------------------------------- dtype I/O
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+    return (float)v;  // exact widening
+}
+
+// Nearest-even fp32 -> bf16 bit pattern (inputs are finite or inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32 under the default round-to-nearest-even mode
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Load element i of a float tensor stored as dtype DT.
+template <int DT>
+__device__ __forceinline__ float load_f(const void* p, int64_t i) {
+    if constexpr (DT == QLIN_F32) return ((const float*)p)[i];
+    else if constexpr (DT == QLIN_BF16) return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+    else return f16_bits_to_f32(((const uint16_t*)p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_f(void* p, int64_t i, float v) {
+    if constexpr (DT == QLIN_F32) ((float*)p)[i] = v;
+    else if constexpr (DT == QLIN_BF16) ((uint16_t*)p)[i] = (uint16_t)f32_to_bf16_rne(v);
+    else ((uint16_t*)p)[i] = (uint16_t)f32_to_f16_rne(v);
+}
+
+// ------------------------------------------------- small formats (decoding)
+
+// E8M0 scale byte: 2^(b-127). b = 0 is the fp32 subnormal 2^-127.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// E4M3 (OCP "FN" variant): bias 7, 3 mantissa bits, no inf. Finite codes only.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float mag = e ? __builtin_ldexpf((float)(8u + m), (int)e - 10) : __builtin_ldexpf((float)m, -9);
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// E2M1: bias 1, 1 mantissa bit; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    float mag = e ? __builtin_ldexpf((float)(2u + m), (int)e - 2) : 0.5f * (float)m;
+    return (c & 8u) ? -mag : mag;
+}
+
+// Byte Q of v holds two E2M1 codes (low nibble first); returns them times
+// `scale` as packed bf16 (exact). The gfx950 scaled-convert instructions
+// apply only the exponent of their scale operand, so arbitrary (E4M3)
+// scales are applied by an fp32 multiply after a unit-scale decode.
+template <int Q>
+__device__ __forceinline__ uint32_t e2m1_pair_times(uint32_t v, float scale) {
+    const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, Q);
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    bf16x2_t r = {(__bf16)(f[0] * scale), (__bf16)(f[1] * scale)};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// ----------------------------------------------------------- launchers
+
+struct QmmArgs {
+    const void* x;       // [rows of A, K]
+    const uint32_t* wq;  // packed weight (expert 0)
+    const void* scales;
+    const void* biases;
+    void* y;
+    int64_t M, N, K;
+    int x_dtype, scale_dtype;
+    int transpose, group_size, bits, mode;
+    // gather form (all zero / null for a plain matmul)
+    int64_t batch_x;             // B
+    int64_t R;                   // rows of the index arrays
+    int64_t E;
+    const uint32_t* lhs;         // [R] or null
+    const uint32_t* rhs;         // [R] or null
+};
+
+hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int g,
+                           int bits, int mode, uint32_t* wq, void* scales, void* biases,
+                           hipStream_t s);
+hipError_t launch_dequantize(const uint32_t* wq, const void* scales, const void* biases,
+                             int sdtype, int64_t rows, int64_t cols, int g, int bits, int mode,
+                             void* out, int out_dtype, hipStream_t s);
+// fp32 VALU path: any dtype, layout and mode; gather form if a.R > 0.
+hipError_t launch_qmm_generic(const QmmArgs& a, hipStream_t s);
+// MFMA small-M path (M <= 16, transpose, bf16 x). Returns hipErrorNotSupported
+// for shapes it does not take.
+hipError_t launch_qmm_decode(const QmmArgs& a, hipStream_t s);
+// MFMA LDS-tiled path (transpose, bf16 x), plain or gathered rows.
+hipError_t launch_qmm_tiled(const QmmArgs& a, const uint32_t* row_perm,
+                            const uint32_t* expert_offsets, hipStream_t s);
+bool qmm_tiled_supports(const QmmArgs& a);
+bool qmm_decode_supports(const QmmArgs& a);
+// MoE bucketing: counts rows per expert, scans, and writes the stable
+// permutation of rows sorted by expert (skipped when rows are pre-sorted).
+hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, int sorted,
+                         void* workspace, uint32_t** row_perm, uint32_t** expert_offsets,
+                         hipStream_t s);
+size_t bucket_workspace_bytes(int64_t R, int64_t E);
+
+}  // namespace qlin

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Bars: codes, packed words, scales and biases bit-exact; dequantized values
+bit-exact; matmul outputs within normwise max relative error 1e-5*sqrt(K)
+(fp32 outputs) or 2e-2 (bf16/f16 outputs). Every input is seeded synthetic
+data drawn by ``synth``.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import ORACLE_DT, from_bits, normwise_rel_err, to_oracle, tolerance
+
+pytestmark = pytest.mark.gpu
+
+qm = pytest.importorskip("quantized_matmul_amd")
+
+DEV = "cuda:0"
+AFFINE_CASES = [(2, 32), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)]
+MICRO_CASES = [("mxfp4", 32, 4), ("mxfp8", 32, 8), ("nvfp4", 16, 4)]
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.fixture(autouse=True)
+def _no_forced_path():
+    os.environ.pop("QLIN_FORCE_PATH", None)
+    yield
+    os.environ.pop("QLIN_FORCE_PATH", None)
+
+
+def gpu_weight(shape, std, wid, dtype):
+    t, bits = synth.normal(shape, std, wid, synth.WEIGHT, dtype)
+    return t.to(DEV), bits
+
+
+def quantize_both(w_gpu, w_bits, dtype, g, b, mode, transpose=True):
+    qw = qm.quantize(w_gpu, g, b, mode, transpose=transpose)
+    ref = oracle.quantize(w_bits, dtype, g, b, mode)
+    return qw, ref
+
+
+# ---------------------------------------------------------------- quantize
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_quantize_affine_bit_exact(dtype, bits, g):
+    print(f"quantize affine {dtype} b{bits} g{g}", flush=True)
+    w, wb = gpu_weight((37, 512), 0.02, 11, dtype)      # ragged row count
+    qw, (wq, sc, bi) = quantize_both(w, wb, dtype, g, bits, "affine")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_oracle(qw.value), wq)
+    assert np.array_equal(to_oracle(qw.scales), sc)
+    assert np.array_equal(to_oracle(qw.biases), bi)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_quantize_micro_bit_exact(dtype, mode, g, bits):
+    print(f"quantize {mode} {dtype}", flush=True)
+    w, wb = gpu_weight((29, 512), 0.02, 12, dtype)
+    qw, (wq, sc, _) = quantize_both(w, wb, dtype, g, bits, mode)
+    torch.cuda.synchronize()
+    assert qw.biases is None
+    assert np.array_equal(to_oracle(qw.scales), sc)
+    assert np.array_equal(to_oracle(qw.value), wq)
+
+
+def test_quantize_special_values_bit_exact():
+    """Constant groups, signed zeros, tiny and large magnitudes, exact ties."""
+    r = np.random.default_rng(5)
+    a = np.zeros((8, 128), np.float32)
+    a[0] = 0.25                                   # constant group
+    a[1, :64] = -0.0
+    a[1, 64:] = 0.0
+    a[2] = r.standard_normal(128) * 1e-30         # subnormal-scale groups
+    a[3] = r.standard_normal(128) * 1e30
+    a[4] = np.tile(np.array([0, 0.5, 1, 1.5, 2, 2.5, 3, 3.5, 5, 6, 7], np.float32), 12)[:128]
+    a[5] = np.arange(128, dtype=np.float32) - 64
+    a[6] = r.integers(-3, 4, 128)
+    a[7] = r.standard_normal(128) * 300
+    for dtype in ("f32", "bf16"):
+        t, bits = synth.as_dtype(a, dtype)
+        for (mode, g, b) in [("affine", 32, 4), ("affine", 64, 2), ("affine", 128, 8)] + MICRO_CASES:
+            qw, (wq, sc, bi) = quantize_both(t.to(DEV), bits, dtype, g, b, mode)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_oracle(qw.value), wq), (dtype, mode)
+            assert np.array_equal(to_oracle(qw.scales), sc), (dtype, mode)
+            if bi is not None:
+                assert np.array_equal(to_oracle(qw.biases), bi), (dtype, mode)
+
+
+# ---------------------------------------------------------------- dequantize
+
+@pytest.mark.parametrize("sdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("odtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 128)])
+def test_dequantize_affine_bit_exact(sdtype, odtype, bits, g):
+    w, wb = gpu_weight((19, 256), 0.5, 13, sdtype)
+    qw, (wq, sc, bi) = quantize_both(w, wb, sdtype, g, bits, "affine")
+    d = qm.dequantize(qw, TDT[odtype])
+    ref = oracle.dequantize(wq, sc, bi, g, bits, "affine", sdtype, odtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_oracle(d), ref)
+
+
+@pytest.mark.parametrize("odtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_dequantize_micro_bit_exact(odtype, mode, g, bits):
+    w, wb = gpu_weight((19, 256), 0.5, 14, "bf16")
+    qw, (wq, sc, _) = quantize_both(w, wb, "bf16", g, bits, mode)
+    d = qm.dequantize(qw, TDT[odtype])
+    ref = oracle.dequantize(wq, sc, None, g, bits, mode, "u8", odtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_oracle(d), ref)
+
+
+def test_roundtrip_rs_example():
+    """mlx-rs test_quantize_dequantize shapes and bound, on the GPU."""
+    x = torch.arange(512, dtype=torch.float32).repeat(128, 1).to(DEV)
+    for b in (2, 4, 8):
+        qw = qm.quantize(x, 128, b)
+        assert tuple(qw.value.shape) == (128, 512 // (32 // b))
+        assert tuple(qw.scales.shape) == (128, 4) and tuple(qw.biases.shape) == (128, 4)
+        xh = qm.dequantize(qw)
+        assert float((x - xh).abs().max()) <= 127.0 / (1 << b)
+
+
+# ---------------------------------------------------------------- matmul
+
+def run_qmm_case(M, N, K, bits, g, mode, xdtype, transpose, path=None, wid=20, std=0.02):
+    wdt = xdtype if mode == "affine" else "bf16"
+    wshape = (N, K) if transpose else (K, N)
+    w, wb = gpu_weight(wshape, std, wid, wdt)
+    xt, xb = synth.normal((M, K), 1.0, wid, synth.ACT, xdtype)
+    qw, (wq, sc, bi) = quantize_both(w, wb, wdt, g, bits, mode, transpose)
+    if path:
+        os.environ["QLIN_FORCE_PATH"] = path
+    y = qm.quantized_matmul(xt.to(DEV), qw)
+    torch.cuda.synchronize()
+    os.environ.pop("QLIN_FORCE_PATH", None)
+    yref = oracle.quantized_matmul(xb, xdtype, wq, sc, bi, transpose, g, bits, mode,
+                                   scale_dtype=(wdt if mode == "affine" else "u8"))
+    assert y.shape == (M, N) and y.dtype == TDT[xdtype]
+    err = normwise_rel_err(y, yref)
+    tol = tolerance(TDT[xdtype], K)
+    print(f"qmm M{M} N{N} K{K} b{bits} g{g} {mode} {xdtype} t{int(transpose)} path={path}: "
+          f"err {err:.3e} tol {tol:.1e}", flush=True)
+    assert err <= tol
+    return err
+
+
+def test_tiny_affine_config():
+    """W f32 [256,512] ~N(0,0.02) int4 g64, x f32 [4,512] ~N(0,1):
+    quantize -> dequantize -> quantized_matmul."""
+    w, wb = gpu_weight((256, 512), 0.02, 1, "f32")
+    xt, xb = synth.normal((4, 512), 1.0, 1, synth.ACT, "f32")
+    qw, (wq, sc, bi) = quantize_both(w, wb, "f32", 64, 4, "affine")
+    d = qm.dequantize(qw)
+    y = qm.quantized_matmul(xt.to(DEV), qw)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_oracle(qw.value), wq)
+    assert np.array_equal(to_oracle(d), oracle.dequantize(wq, sc, bi, 64, 4, scale_dtype="f32"))
+    yref = oracle.quantized_matmul(xb, "f32", wq, sc, bi, True, 64, 4)
+    assert normwise_rel_err(y, yref) <= 1e-5 * np.sqrt(512)
+
+
+@pytest.mark.parametrize("M", [1, 3, 4, 8, 16])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_decode_kernel_affine(M, bits, g):
+    if bits == 2 and g == 32 and M > 8:
+        pytest.skip("2-bit g32 decode kernel takes M <= 8 (other paths cover it)")
+    run_qmm_case(M, 80, 1024, bits, g, "affine", "bf16", True, path="decode", wid=21 + bits)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_decode_kernel_micro(M, mode, g, bits):
+    run_qmm_case(M, 48, 1024, bits, g, mode, "bf16", True, path="decode", wid=31)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 128, 256), (100, 200, 512), (256, 256, 192), (300, 64, 256)])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_tiled_kernel_affine(M, N, K, bits, g):
+    if K % g:
+        pytest.skip("group does not divide K")
+    run_qmm_case(M, N, K, bits, g, "affine", "bf16", True, path="tiled", wid=71 + bits)
+
+
+@pytest.mark.parametrize("M", [17, 260])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_tiled_kernel_micro(M, mode, g, bits):
+    run_qmm_case(M, 136, 512, bits, g, mode, "bf16", True, path="tiled", wid=72)
+
+
+@pytest.mark.parametrize("transpose", [True, False])
+@pytest.mark.parametrize("xdtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 128)])
+def test_generic_kernel_affine(transpose, xdtype, bits, g):
+    run_qmm_case(5, 128, 256, bits, g, "affine", xdtype, transpose, path="generic", wid=41)
+
+
+@pytest.mark.parametrize("transpose", [True, False])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_generic_kernel_micro(transpose, mode, g, bits):
+    run_qmm_case(3, 128, 256, bits, g, mode, "bf16", transpose, path="generic", wid=42)
+
+
+def test_rs_quantized_matmul_example_gpu():
+    """mlx-rs test_quantized_matmul: transpose=false, g64 b4, max diff < 1e-3."""
+    m, n, k = 32, 128, 128
+    xt, xb = synth.normal((m, k), 1 / np.sqrt(k), 1001, 1, "f32")
+    wt, wb = synth.normal((k, n), 1 / np.sqrt(k), 1001, 0, "f32")
+    qw = qm.quantize(wt.to(DEV), 64, 4, transpose=False)
+    w_hat = qm.dequantize(qw)
+    y_q = qm.quantized_matmul(xt.to(DEV), qw)
+    y_hat = xt.to(DEV) @ w_hat
+    torch.cuda.synchronize()
+    assert y_q.shape == y_hat.shape
+    assert float((y_q - y_hat).abs().max()) < 1e-3
+
+
+def test_page_worked_example_shape():
+    """"Emily.Quantization.Layers" example: x iota {2,128} . W iota {4,128} -> {2,4}."""
+    w = torch.arange(4 * 128, dtype=torch.float32).reshape(4, 128).to(DEV)
+    x = torch.arange(2 * 128, dtype=torch.float32).reshape(2, 128).to(DEV)
+    qw = qm.quantize(w)
+    y = qm.quantized_matmul(x, qw)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 4)
+    wq, sc, bi = oracle.quantize(w.cpu().numpy(), "f32", 64, 4)
+    yref = oracle.quantized_matmul(x.cpu().numpy(), "f32", wq, sc, bi, True, 64, 4)
+    assert normwise_rel_err(y, yref) <= 1e-5 * np.sqrt(128)
+
+
+def test_edge_empty_and_ragged():
+    w, wb = gpu_weight((50, 256), 0.02, 51, "bf16")          # N = 50: ragged column blocks
+    qw, (wq, sc, bi) = quantize_both(w, wb, "bf16", 64, 4, "affine")
+    x0 = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    assert qm.quantized_matmul(x0, qw).shape == (0, 50)
+    xt, xb = synth.normal((2, 3, 256), 1.0, 51, 1, "bf16")  # batch dims flattened
+    y = qm.quantized_matmul(xt.to(DEV), qw)
+    torch.cuda.synchronize()
+    yref = oracle.quantized_matmul(xb.reshape(6, 256), "bf16", wq, sc, bi, True, 64, 4)
+    assert y.shape == (2, 3, 50)
+    assert normwise_rel_err(y.reshape(6, 50), yref) <= 2e-2
+    # K that the decode kernel's 128-wide units do not tile (falls back)
+    run_qmm_case(2, 40, 192, 4, 64, "affine", "bf16", True, wid=52)
+
+
+# ---------------------------------------------------------------- gather
+
+def run_gather_case(B, M, K, N, E, rhs, lhs, bits=4, g=64, mode="affine", xdtype="bf16",
+                    transpose=True, sorted_indices=False, path=None, wid=60):
+    wdt = xdtype if mode == "affine" else "bf16"
+    wshape = (E, N, K) if transpose else (E, K, N)
+    w, wb = gpu_weight(wshape, 0.02, wid, wdt)
+    xt, xb = synth.normal((B, M, K), 1.0, wid, synth.ACT, xdtype)
+    qw, (wq, sc, bi) = quantize_both(w, wb, wdt, g, bits, mode, transpose)
+    rhs_t = torch.tensor(np.asarray(rhs), dtype=torch.int32)
+    lhs_t = None if lhs is None else torch.tensor(np.asarray(lhs), dtype=torch.int32)
+    if path:
+        os.environ["QLIN_FORCE_PATH"] = path
+    y = qm.gather_qmm(xt.to(DEV), qw, rhs_t.to(DEV), None if lhs_t is None else lhs_t.to(DEV),
+                      sorted_indices=sorted_indices)
+    torch.cuda.synchronize()
+    os.environ.pop("QLIN_FORCE_PATH", None)
+    rhs_f = np.asarray(rhs, np.uint32).ravel()
+    lhs_f = None if lhs is None else np.broadcast_to(np.asarray(lhs, np.uint32), np.asarray(rhs).shape).ravel()
+    yref = oracle.gather_qmm(xb, xdtype, wq, sc, bi, rhs_f, lhs_f, transpose, g, bits, mode,
+                             scale_dtype=(wdt if mode == "affine" else "u8"))
+    err = normwise_rel_err(y.reshape(yref.shape), yref)
+    print(f"gather B{B} M{M} K{K} N{N} E{E} R{rhs_f.size} {mode} b{bits} t{int(transpose)} "
+          f"sorted={sorted_indices} path={path}: err {err:.3e}", flush=True)
+    assert err <= tolerance(TDT[xdtype], K)
+
+
+def test_gather_rs_cases():
+    """mlx-rs test_gather_qmm index cases (fp32, allclose 1e-4 there)."""
+    run_gather_case(1, 32, 64, 64, 3, [2, 1], [0], xdtype="f32", wid=61)
+    run_gather_case(5, 32, 64, 64, 3, [2, 1], [0, 2], xdtype="f32", wid=62)
+
+
+@pytest.mark.parametrize("sorted_indices", [False, True])
+def test_gather_moe_small(sorted_indices):
+    T, E, k = 24, 8, 3
+    rhs = synth.topk_distinct(T, E, k, 63)
+    if sorted_indices:
+        order = np.argsort(rhs.ravel(), kind="stable")
+        rhs_s = rhs.ravel()[order]
+        lhs = (order // k).astype(np.uint32)
+        run_gather_case(T, 1, 256, 128, E, rhs_s, lhs, sorted_indices=True, wid=63)
+    else:
+        lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+        run_gather_case(T, 1, 256, 128, E, rhs, lhs, wid=63)
+
+
+def test_gather_identity_lhs_and_micro():
+    run_gather_case(6, 2, 256, 64, 4, [3, 0, 1, 3, 2, 0], None, wid=64)
+    run_gather_case(6, 2, 256, 64, 4, [3, 0, 1, 3, 2, 0], None, bits=4, g=32, mode="mxfp4", wid=65)
+    run_gather_case(6, 2, 256, 64, 4, [1, 1, 0, 3, 2, 0], None, transpose=False, wid=66)
+
+
+@pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8)] + MICRO_CASES)
+def test_gather_tiled_modes(mode, g, bits):
+    T, E, k = 40, 6, 2
+    rhs = synth.topk_distinct(T, E, k, 68)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+    run_gather_case(T, 3, 256, 200, E, rhs, lhs, bits=bits, g=g, mode=mode, wid=68)
+
+
+def test_gather_skewed_experts():
+    """One hot expert with 150 rows (several row tiles), several empty ones."""
+    rhs = np.array([5] * 150 + [0] * 3 + [2] * 70, np.uint32)
+    np.random.default_rng(3).shuffle(rhs)
+    run_gather_case(rhs.size, 1, 128, 96, 9, rhs, None, wid=69)
+    order = np.argsort(rhs, kind="stable")
+    run_gather_case(rhs.size, 1, 128, 96, 9, rhs[order], order.astype(np.uint32),
+                    sorted_indices=True, wid=69)
+
+
+def test_gather_sorted_flag_is_only_a_hint():
+    """Flag set on indices that are not sorted: results must not change."""
+    run_gather_case(6, 1, 256, 64, 4, [3, 0, 1, 3, 2, 0], None, sorted_indices=True, wid=67)
