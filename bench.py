@@ -1,0 +1,294 @@
+"""Benchmark: quantized matmul on one MI355X.
+
+Headline (one JSON line on stdout): decode quantized_matmul GB/s on the
+int4 group-64 affine weight W [14336, 4096] (bf16 scales/biases, [out, in]
+layout) with x bf16 [1, 4096] -- one step is one fused quantized matmul
+over one token. The second half of the metric (prefill TFLOP/s, x bf16
+[2048, 4096] against W [12288, 4096]) and every other workload shape are
+measured in the same run and reported alongside.
+
+Timing: inputs resident in HBM; decode steps cycle through >= 512 MB of
+distinct weight copies so that the 256 MB Infinity Cache cannot serve them;
+the timed launches are captured in a HIP graph (no host overhead between
+kernels) and bracketed by torch.cuda.synchronize() and HIP events on the
+launch stream. Algorithmic bytes = packed W + scales + biases + x + y, each
+counted once; flops = 2*M*N*K.
+
+cpu_baseline: the CPU oracle (test infrastructure, plain C, fp64) on a
+bounded sample of the same decode workload, timed on this host.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qmm decode GB/s (% of HBM peak) + prefill TFLOP/s; int4 g64 affine"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
+ROTATE_BYTES = 512 * 2 ** 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--only", choices=["all", "decode", "prefill", "headline"], default="all")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain device copy of known size (counter scaling)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(the sharded form is described in DESIGN.md)"}))
+        sys.exit(2)
+
+    import torch
+    import quantized_matmul_amd as qm
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ helpers
+    def qw_bytes(qw):
+        b = qw.value.numel() * 4 + qw.scales.numel() * qw.scales.element_size()
+        if qw.biases is not None:
+            b += qw.biases.numel() * qw.biases.element_size()
+        return b
+
+    def clone_qw(qw):
+        return qm.QuantizedWeight(qw.value.clone(), qw.scales.clone(),
+                                  None if qw.biases is None else qw.biases.clone(),
+                                  qw.group_size, qw.bits, qw.transpose, qw.mode)
+
+    def make_weight(shape, wid, mode, g, bits, transpose):
+        w, _ = synth.normal(shape, 0.02, wid, synth.WEIGHT, "bf16")
+        qw = qm.quantize(w.to(dev), g, bits, mode, transpose=transpose)
+        del w
+        return qw
+
+    def timed(fn_list, steps, warmup, graph=True):
+        """Run fn_list[s % len] for `steps` steps; returns seconds per step."""
+        stream = torch.cuda.current_stream()
+        for s in range(warmup):
+            fn_list[s % len(fn_list)]()
+        torch.cuda.synchronize()
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(steps):
+                    fn_list[s % len(fn_list)]()
+            g.replay()  # warm replay
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            del g
+        else:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for s in range(steps):
+                fn_list[s % len(fn_list)]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+        return ms / 1e3 / steps
+
+    # ------------------------------------------------------------ decode
+    def decode_case(M, N, K, bits, g, mode="affine", transpose=True, wid=101, steps=None):
+        shape = (N, K) if transpose else (K, N)
+        qw = make_weight(shape, wid, mode, g, bits, transpose)
+        per = qw_bytes(qw)
+        ncopy = max(1, math.ceil(ROTATE_BYTES / per))
+        copies = [qw] + [clone_qw(qw) for _ in range(ncopy - 1)]
+        x, _ = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
+        x = x.to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fns = [lambda c=c: qm.quantized_matmul(x, c, out=y) for c in copies]
+        n = steps or args.steps
+        n = max(len(fns), (n // len(fns)) * len(fns))
+        sec = timed(fns, n, args.warmup)
+        alg = per + x.numel() * 2 + y.numel() * 2
+        gbs = alg / sec / 1e9
+        del copies, fns
+        torch.cuda.empty_cache()
+        return {"workload": f"decode qmm {mode} {bits}-bit g{g} M{M} N{N} K{K} "
+                            f"transpose={'true' if transpose else 'false'}",
+                "us": sec * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                "TFLOP/s": 2 * M * N * K / sec / 1e12, "alg_bytes": alg, "copies": ncopy,
+                "steps": n}
+
+    def prefill_case(M, N, K, bits, g, mode="affine", wid=201, steps=None):
+        qw = make_weight((N, K), wid, mode, g, bits, True)
+        x, _ = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
+        x = x.to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fns = [lambda: qm.quantized_matmul(x, qw, out=y)]
+        n = steps or max(10, args.steps // 8)
+        sec = timed(fns, n, min(args.warmup, 5))
+        flops = 2 * M * N * K
+        tf = flops / sec / 1e12
+        alg = qw_bytes(qw) + x.numel() * 2 + y.numel() * 2
+        return {"workload": f"prefill qmm {mode} {bits}-bit g{g} M{M} N{N} K{K} transpose=true",
+                "us": sec * 1e6, "TFLOP/s": tf, "frac_mfma": tf / MFMA_PEAK_TFLOPS["bf16"],
+                "GB/s": alg / sec / 1e9, "flops": flops, "alg_bytes": alg, "steps": n}
+
+    def moe_case(sorted_indices, wid=301):
+        E, N, K, T, k = 64, 1536, 2048, 512, 8
+        qw = make_weight((E, N, K), wid, "affine", 64, 4, True)
+        x, _ = synth.normal((T, 1, K), 1.0, wid, synth.ACT, "bf16")
+        x = x.to(dev)
+        rhs = torch.from_numpy(synth.topk_distinct(T, E, k, wid).astype("int32"))
+        lhs = torch.arange(T, dtype=torch.int32).repeat_interleave(k).reshape(T, k)
+        if sorted_indices:
+            order = torch.argsort(rhs.reshape(-1), stable=True)
+            rhs_f, lhs_f = rhs.reshape(-1)[order], lhs.reshape(-1)[order]
+        else:
+            rhs_f, lhs_f = rhs.reshape(-1), lhs.reshape(-1)
+        rhs_f, lhs_f = rhs_f.to(dev), lhs_f.to(dev)
+        R = rhs_f.numel()
+        ws = torch.empty(qm.gather_qmm_workspace_bytes(R, E), dtype=torch.uint8, device=dev)
+        y = torch.empty((R, 1, N), dtype=torch.bfloat16, device=dev)
+        fns = [lambda: qm.gather_qmm(x, qw, rhs_f, lhs_f, sorted_indices=sorted_indices,
+                                     workspace=ws, out=y)]
+        n = max(10, args.steps // 4)
+        sec = timed(fns, n, min(args.warmup, 5))
+        alg = qw_bytes(qw) + x.numel() * 2 + y.numel() * 2 + 2 * R * 4
+        flops = 2 * R * N * K
+        return {"workload": f"MoE gather_qmm affine 4-bit g64 E{E} N{N} K{K} tokens{T} top{k} "
+                            f"sorted={'true' if sorted_indices else 'false'}",
+                "us": sec * 1e6, "GB/s": alg / sec / 1e9, "frac_hbm": alg / sec / 1e9 / HBM_PEAK_GBS,
+                "TFLOP/s": flops / sec / 1e12,
+                "frac_mfma": flops / sec / 1e12 / MFMA_PEAK_TFLOPS["bf16"], "steps": n}
+
+    results = []
+    log("decode headline: affine int4 g64 M1 N14336 K4096")
+    head = decode_case(1, 14336, 4096, 4, 64, wid=101)
+    results.append(head)
+    log(json.dumps(head))
+    pre = None
+    if args.only in ("all", "prefill", "headline"):
+        log("prefill: affine int4 g64 M2048 N12288 K4096")
+        pre = prefill_case(2048, 12288, 4096, 4, 64, wid=201)
+        results.append(pre)
+        log(json.dumps(pre))
+    if args.only in ("all", "decode"):
+        for (M, bits, g, t) in [(4, 4, 64, True), (8, 4, 64, True), (1, 8, 64, True),
+                                (1, 2, 32, True), (1, 4, 64, False), (4, 4, 64, False)]:
+            r = decode_case(M, 14336, 4096, bits, g, transpose=t, wid=110 + bits,
+                            steps=max(32, args.steps // 4))
+            results.append(r)
+            log(json.dumps(r))
+        for mode, g, bits in [("mxfp4", 32, 4), ("nvfp4", 16, 4), ("mxfp8", 32, 8)]:
+            for M in (1, 16):
+                r = decode_case(M, 8192, 8192, bits, g, mode=mode, wid=120,
+                                steps=max(32, args.steps // 4))
+                results.append(r)
+                log(json.dumps(r))
+    if args.only in ("all", "prefill"):
+        r = prefill_case(2048, 12288, 4096, 4, 128, wid=202)
+        results.append(r)
+        log(json.dumps(r))
+        for mode, g, bits in [("mxfp4", 32, 4), ("nvfp4", 16, 4), ("mxfp8", 32, 8)]:
+            r = prefill_case(512, 8192, 8192, bits, g, mode=mode, wid=203)
+            results.append(r)
+            log(json.dumps(r))
+    if args.only == "all":
+        for s in (False, True):
+            r = moe_case(s)
+            results.append(r)
+            log(json.dumps(r))
+    if args.copy_probe:
+        n = 256 * 2 ** 20
+        a = torch.empty(n // 4, dtype=torch.int32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 device copies of {n} bytes")
+
+    # ------------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_seconds, log)
+
+    # ------------------------------------------------------------ headline
+    line = {
+        "metric": METRIC,
+        "value": round(head["GB/s"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["us"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": "decode quantized_matmul, affine int4 group 64, bf16 scales/biases, "
+                               "x bf16 [1,4096], W [14336,4096] ([out,in], transpose=true)",
+                   "M": 1, "N": 14336, "K": 4096, "bits": 4, "group_size": 64, "mode": "affine",
+                   "weight_copies_rotated": head["copies"]},
+        "roofline": {"bound": "hbm", "achieved": round(head["GB/s"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["frac_hbm"], 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        line["prefill"] = {"value": round(pre["TFLOP/s"], 2), "unit": "TFLOP/s",
+                           "workload": pre["workload"],
+                           "roofline": {"bound": "mfma", "achieved": round(pre["TFLOP/s"], 2),
+                                        "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                                        "frac": round(pre["frac_mfma"], 4), "traffic": None}}
+    line["configs"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                       for r in results]
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(seconds, log):
+    """The oracle on the decode workload, timed on this host's cores."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    M, N, K = 1, 14336, 4096
+    _, wb = synth.normal((N, K), 0.02, 101, synth.WEIGHT, "bf16")
+    _, xb = synth.normal((M, K), 1.0, 101, synth.ACT, "bf16")
+    wq, sc, bi = oracle.quantize(wb, "bf16", 64, 4)
+    alg = wq.nbytes + sc.nbytes + bi.nbytes + xb.nbytes + M * N * 2
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantized_matmul(xb, "bf16", wq, sc, bi, True, 64, 4)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"cpu oracle: {calls} full decode calls in {el:.2f}s on {threads} threads")
+    return {"value": round(alg * calls / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} complete oracle quantized_matmul calls on the decode workload "
+                      f"(M1 N{N} K{K} int4 g64), {el:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

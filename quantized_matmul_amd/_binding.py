@@ -145,7 +145,17 @@ def dequantize(qw: QuantizedWeight, dtype: Optional[torch.dtype] = None) -> torc
     return out
 
 
-def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight) -> torch.Tensor:
+def _out(out, shape, dtype, dev):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or not out.is_contiguous() \
+            or out.device != dev:
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {tuple(shape)} on {dev}")
+    return out
+
+
+def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """qlin_quantized_matmul: x [..., K] -> y [..., N] in x's dtype.
 
     W is 2-D: [N, K] packed along K when qw.transpose, else [K, N] packed
@@ -164,7 +174,7 @@ def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight) -> torch.Tensor:
     if x.shape[-1] != K:
         raise ValueError(f"x's last dim {x.shape[-1]} does not match the weight's K={K}")
     M = x.numel() // K if K else 0
-    y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=dev)
+    y = _out(out, tuple(x.shape[:-1]) + (N,), x.dtype, dev)
     rc = lib.qlin_quantized_matmul(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value),
                                    _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype], N,
                                    int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),
@@ -179,7 +189,8 @@ def gather_qmm_workspace_bytes(R: int, E: int) -> int:
 
 def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
                lhs_indices: Optional[torch.Tensor] = None, sorted_indices: bool = False,
-               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+               workspace: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """qlin_gather_qmm: y[r] = x[lhs[r]] . W[rhs[r]]^T (or . W[rhs[r]]).
 
     x [B, M, K]; qw.value stacks experts on its leading axis; rhs_indices
@@ -211,7 +222,7 @@ def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
     need = int(lib.qlin_gather_qmm_workspace_bytes(R, E))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    y = torch.empty(shape + (M, N), dtype=x.dtype, device=dev)
+    y = _out(out, shape + (M, N), x.dtype, dev)
     rc = lib.qlin_gather_qmm(_ptr(x), _DTYPE[x.dtype], B, M, K, _ptr(qw.value), _ptr(qw.scales),
                              _ptr(qw.biases), _DTYPE[qw.scales.dtype], E, N, _ptr(lhs), _ptr(rhs),
                              R, int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),

@@ -79,19 +79,21 @@ struct Fmt {
     static constexpr float OFF = (AFF && BITS != 8) ? 128.0f : 0.0f;  // code offset
     static constexpr int WPU = (RPU * SPR) / WS;   // affine windows per unit
     static constexpr int STEPS = RPU * SPR;        // MFMA K-steps per unit
+    // x elements per fragment-order permutation block
+    static constexpr int XBLOCK = (BITS == 4) ? 8 : (BITS == 8 ? 32 : 64);
 
     // k (within the 32- or 64-wide block of global step gs) of element e of
     // the A/B fragment held by lane row j. Must match unpack() below.
     __device__ static int chunk_k(int gs, int j, int e) {
         if constexpr (BITS == 4 && AFF) {
-            const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+            const int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
             return 8 * (4 * gs + j) + perm[e];
         } else if constexpr (BITS == 4) {
             return 8 * (4 * gs + j) + e;  // fp4 pairs decode in natural order
         } else if constexpr (BITS == 8) {
             return 32 * gs + (e < 4 ? 4 * j + e : 16 + 4 * j + (e - 4));
         } else {  // 2-bit: steps (c, h) of a 64-wide block b, gs = 2b + h
-            const int perm[2][8] = {{0, 8, 1, 9, 2, 10, 3, 11}, {4, 12, 5, 13, 6, 14, 7, 15}};
+            const int perm[2][8] = {{0, 4, 1, 5, 2, 6, 3, 7}, {8, 12, 9, 13, 10, 14, 11, 15}};
             int b = gs >> 1, h = gs & 1;
             return 16 * (4 * b + j) + perm[h][e];
         }
@@ -105,18 +107,23 @@ template <int MODE, int BITS, int G>
 __device__ __forceinline__ u32x4 unpack(const u32x4& w, int t, float sc) {
     u32x4 b;
     if constexpr (MODE == AFFINE && BITS == 4) {
-        const uint32_t v = w[t], M4 = 0x000F000Fu, MAG = 0x43004300u;
-        b[0] = (v & M4) | MAG;
-        b[1] = ((v >> 4) & M4) | MAG;
-        b[2] = ((v >> 8) & M4) | MAG;
-        b[3] = ((v >> 12) & M4) | MAG;
+        // nibbles -> bytes (even / odd codes), then v_perm pairs each code
+        // byte with 0x43: bf16 0x43nn = 128 + nn exactly.
+        const uint32_t v = w[t], C = 0x43434343u;
+        const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+        b[0] = __builtin_amdgcn_perm(C, lo, 0x04010400u);  // codes 0, 2
+        b[1] = __builtin_amdgcn_perm(C, lo, 0x04030402u);  // codes 4, 6
+        b[2] = __builtin_amdgcn_perm(C, hi, 0x04010400u);  // codes 1, 3
+        b[3] = __builtin_amdgcn_perm(C, hi, 0x04030402u);  // codes 5, 7
     } else if constexpr (MODE == AFFINE && BITS == 2) {
-        const uint32_t v = w[t >> 1], M2 = 0x00030003u, MAG = 0x43004300u;
-        const int s0 = (t & 1) * 4;  // pairs (s, s+8) for s = s0 .. s0+3
-        b[0] = ((v >> (2 * s0)) & M2) | MAG;
-        b[1] = ((v >> (2 * s0 + 2)) & M2) | MAG;
-        b[2] = ((v >> (2 * s0 + 4)) & M2) | MAG;
-        b[3] = ((v >> (2 * s0 + 6)) & M2) | MAG;
+        // 2-bit codes s, s+4, s+8, s+12 in the bytes of (v >> 2s) & 0x03030303;
+        // step half h takes byte pairs (0,1) or (2,3) of the four masks.
+        const uint32_t v = w[t >> 1], C = 0x43434343u;
+        const uint32_t sel = (t & 1) ? 0x04030402u : 0x04010400u;
+        b[0] = __builtin_amdgcn_perm(C, v & 0x03030303u, sel);
+        b[1] = __builtin_amdgcn_perm(C, (v >> 2) & 0x03030303u, sel);
+        b[2] = __builtin_amdgcn_perm(C, (v >> 4) & 0x03030303u, sel);
+        b[3] = __builtin_amdgcn_perm(C, (v >> 6) & 0x03030303u, sel);
     } else if constexpr (MODE == AFFINE && BITS == 8) {
         // byte -> fp32 (v_cvt_f32_ubyteN) -> packed bf16 (v_cvt_pk_bf16_f32); exact
         const uint32_t va = w[2 * t], vb = w[2 * t + 1];
@@ -171,35 +178,161 @@ struct DecodeArgs {
 // padded by 16 bytes, then the cross-wave reduction buffer.
 __host__ __device__ constexpr int xrow_bytes(int K) { return K * 2 + 16; }
 
-template <int MODE, int BITS, int G, int CB, int KS, int MREG, int PF>
-__global__ void __launch_bounds__(64 * KS) qmm_decode_kernel(DecodeArgs a) {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait for this wave's LDS operations only (vector-memory loads may stay in
+// flight), then a workgroup barrier without the memory fence __syncthreads
+// implies: the weight loads issued before it keep streaming.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ u32x4 interleave16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1) {
+    // (a0.lo, b0.lo), (a0.hi, b0.hi), (a1.lo, b1.lo), (a1.hi, b1.hi)
+    return u32x4{__builtin_amdgcn_perm(b0, a0, 0x05040100u), __builtin_amdgcn_perm(b0, a0, 0x07060302u),
+                 __builtin_amdgcn_perm(b1, a1, 0x05040100u), __builtin_amdgcn_perm(b1, a1, 0x07060302u)};
+}
+
+// Write one block of x (natural order, in registers) to LDS in fragment
+// order (the k order chunk_k() defines). Blocks: 8 elements (4-bit), 32
+// (8-bit: chunk j = pieces j and 4+j of 4 elements), 64 (2-bit).
+template <int MODE, int BITS>
+__device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v) {
+    constexpr bool AFF = MODE == AFFINE;
+    if constexpr (BITS == 4 && !AFF) {
+        dst[0] = v[0];  // fp4 pairs decode in natural order
+    } else if constexpr (BITS == 4) {
+        // (x0,x2), (x4,x6), (x1,x3), (x5,x7)
+        const u32x4 c = v[0];
+        dst[0] = u32x4{__builtin_amdgcn_perm(c[1], c[0], 0x05040100u),
+                       __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
+                       __builtin_amdgcn_perm(c[1], c[0], 0x07060302u),
+                       __builtin_amdgcn_perm(c[3], c[2], 0x07060302u)};
+    } else if constexpr (BITS == 8) {
+        const u32x4 c0 = v[0], c1 = v[1], c2 = v[2], c3 = v[3];
+        dst[0] = u32x4{c0[0], c0[1], c2[0], c2[1]};
+        dst[1] = u32x4{c0[2], c0[3], c2[2], c2[3]};
+        dst[2] = u32x4{c1[0], c1[1], c3[0], c3[1]};
+        dst[3] = u32x4{c1[2], c1[3], c3[2], c3[3]};
+    } else {
+        // 16-element word segment jj = natural chunks (2jj, 2jj+1); fragment
+        // chunk 4h + jj = natural chunk 2jj + h as (x0,x4),(x1,x5),(x2,x6),(x3,x7)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 c = v[2 * jj + h];
+                dst[4 * h + jj] = interleave16(c[0], c[1], c[2], c[3]);
+            }
+    }
+}
+
+// Workgroup: KS waves, wave w owning K-slice [w*UPW*U, (w+1)*UPW*U) of one
+// 16-column block. A wave first issues its scale data and its slice of x
+// (ordinary loads, before any weight), then the first PF weight units; it
+// writes its x slice into its own columns of the LDS x rows (already in
+// fragment order) and streams the remaining units through a PF-deep ring,
+// waiting only for the oldest unit. Waves meet once, for the final
+// cross-wave sum.
+template <int MODE, int BITS, int G, int UPW, int PF, int MREG>
+__global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
+    constexpr int KW = UPW * F::U;                 // k per wave
     extern __shared__ __align__(16) unsigned char smem[];
+    const int KS = (int)(blockDim.x >> 6);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int i = lane & 15, j = lane >> 4;
     const int K = a.K, M = a.M;
     const int rowb = xrow_bytes(K);
-    const int nchunks = K / 8;
+    float* red = (float*)(smem + (M + 1) * rowb);  // [KS][16 rows][16 cols]
 
-    // ---- stage x into LDS in fragment order (row M = zeros)
-    for (int idx = tid; idx < (M + 1) * nchunks; idx += 64 * KS) {
-        const int r = idx / nchunks, q = idx - r * nchunks;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < M) {
-            const int gs = q >> 2, jj = q & 3;
-            const uint16_t* xr = a.x + (size_t)r * K;
-            uint32_t h[8];
+    const int k0 = wv * KW;                       // first k of this wave
+    const int u_begin = wv * UPW;
+    const int n0 = blockIdx.x * 16;
+    const int wpr = K / F::PER;                   // words per weight row
+    const int gpr = K / G;                        // groups per weight row
+    const int ncol = min(n0 + i, a.N - 1);        // ragged N: re-read the last row, never stored
+    const uint32_t* wrow = a.wq + (size_t)ncol * wpr + 4 * j;
+    const size_t rowg = (size_t)ncol * gpr;
+
+    // ---- 1. scale data of the slice (contiguous in the row)
+    constexpr int SB = F::AFF ? UPW * F::GPU * 2 : UPW * F::GPU;  // bytes per slice
+    constexpr int SW = (SB + 3) / 4;
+    uint32_t sraw[SW], zraw[F::AFF ? SW : 1];
+    {
+        const size_t gfirst = rowg + (size_t)u_begin * F::GPU;
+        const unsigned char* sp = F::AFF ? (const unsigned char*)a.scales + gfirst * 2
+                                         : (const unsigned char*)a.scales + gfirst;
+        const unsigned char* zp = (const unsigned char*)a.biases + gfirst * 2;
+        if constexpr (SB >= 16) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = xr[F::chunk_k(gs, jj, e)];
-            v[0] = h[0] | (h[1] << 16);
-            v[1] = h[2] | (h[3] << 16);
-            v[2] = h[4] | (h[5] << 16);
-            v[3] = h[6] | (h[7] << 16);
+            for (int v = 0; v < SB / 16; ++v) {
+                const u32x4 t = *(const u32x4*)(sp + 16 * v);
+                sraw[4 * v] = t[0]; sraw[4 * v + 1] = t[1]; sraw[4 * v + 2] = t[2]; sraw[4 * v + 3] = t[3];
+                if constexpr (F::AFF) {
+                    const u32x4 tz = *(const u32x4*)(zp + 16 * v);
+                    zraw[4 * v] = tz[0]; zraw[4 * v + 1] = tz[1]; zraw[4 * v + 2] = tz[2]; zraw[4 * v + 3] = tz[3];
+                }
+            }
+        } else if constexpr (SB == 8) {
+            const uint2 t = *(const uint2*)sp;
+            sraw[0] = t.x; sraw[1] = t.y;
+            if constexpr (F::AFF) { const uint2 tz = *(const uint2*)zp; zraw[0] = tz.x; zraw[1] = tz.y; }
+        } else if constexpr (SB == 4) {
+            sraw[0] = *(const uint32_t*)sp;
+            if constexpr (F::AFF) zraw[0] = *(const uint32_t*)zp;
+        } else {
+            sraw[0] = *(const uint16_t*)sp;
+            if constexpr (F::AFF) zraw[0] = *(const uint16_t*)zp;
         }
-        *(u32x4*)(smem + r * rowb + q * 16) = v;
     }
-    float* red = (float*)(smem + (M + 1) * rowb);  // [KS][CB][16 rows][16 cols]
-    __syncthreads();
+
+    // ---- 2. this wave's x slice: M rows x KW elements, in blocks of BE
+    // elements (the unit of the fragment-order permutation), spread over the
+    // lanes; 16-byte chunks, at most XPL per lane
+    constexpr int BE = F::XBLOCK;                  // elements per permutation block
+    constexpr int CPB = BE / 8;                    // chunks per block
+    constexpr int XPL = 8;                         // chunk registers per lane
+    const int xchunks = M * (KW / 8);              // host guarantees <= 64 * XPL
+    u32x4 xr[XPL];
+#pragma unroll
+    for (int c = 0; c < XPL; ++c) {
+        // chunk id: lane-major within blocks so one lane owns whole blocks
+        const int blk = (c / CPB) * 64 + lane, part = c % CPB;
+        const int cid = blk * CPB + part;
+        xr[c] = u32x4{0u, 0u, 0u, 0u};
+        if (cid < xchunks) {
+            const int m = cid / (KW / 8), q = cid - m * (KW / 8);
+            xr[c] = *(const u32x4*)(a.x + (size_t)m * K + k0 + q * 8);
+        }
+    }
+
+    // ---- 3. the first PF weight units
+    u32x4 wbuf[PF][F::RPU];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < UPW) {
+#pragma unroll
+            for (int r = 0; r < F::RPU; ++r)
+                wbuf[p][r] = *(const u32x4*)(wrow + (size_t)((u_begin + p) * F::RPU + r) * 16);
+        }
+
+    // ---- 4. x slice -> LDS (fragment order) + this slice of the zero row
+#pragma unroll
+    for (int c = 0; c < XPL; c += CPB) {
+        const int blk = (c / CPB) * 64 + lane;
+        const int cid = blk * CPB;
+        if (cid < xchunks) {
+            const int m = cid / (KW / 8), q = cid - m * (KW / 8);
+            u32x4* dst = (u32x4*)(smem + m * rowb + (k0 / 8 + q) * 16);
+            store_fragment_block<MODE, BITS>(dst, &xr[c]);
+        }
+    }
+    for (int q = lane; q < KW / 8; q += 64)
+        *(u32x4*)(smem + M * rowb + (k0 / 8 + q) * 16) = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (loads stay in flight)
+    __builtin_amdgcn_wave_barrier();
 
     // ---- this lane's A row (zero row when it carries no real x row)
     int arow;
@@ -207,143 +340,130 @@ __global__ void __launch_bounds__(64 * KS) qmm_decode_kernel(DecodeArgs a) {
     else arow = (i < M) ? i : M;
     const unsigned char* abase = smem + arow * rowb + j * 16;
 
-    // ---- K-slice of this wave, in units of F::U
-    const int nunits = K / F::U;
-    const int u0 = (wv * nunits) / KS, u1 = ((wv + 1) * nunits) / KS;
-    const int n0 = blockIdx.x * (16 * CB);
-    const int wpr = K / F::PER;           // words per weight row
-    const int gpr = K / G;                // groups per weight row
-    const uint32_t* wrow[CB];
-    int ncol[CB];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dsum = {0.f, 0.f, 0.f, 0.f};
+    float ysum[MREG];
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-        int n = n0 + 16 * c + i;
-        ncol[c] = n < a.N ? n : a.N - 1;  // ragged N: re-read the last row, never stored
-        wrow[c] = a.wq + (size_t)ncol[c] * wpr + 4 * j;
-    }
+    for (int r = 0; r < MREG; ++r) ysum[r] = 0.f;
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // prefetch ring: PF units of weights and scale data per column block.
-    // Affine: per window, the scale/bias (bf16 bits) of this lane's group.
-    // Microscaled: per K-step, the scale byte of this lane's 8 codes.
-    constexpr int NSC = F::AFF ? F::WPU : F::STEPS;
-    u32x4 wbuf[PF][CB][F::RPU];
-    uint32_t sbuf[PF][CB][NSC];
-    uint32_t zbuf[PF][CB][F::AFF ? NSC : 1];
-    auto issue = [&](int slot, int u) {
 #pragma unroll
-        for (int c = 0; c < CB; ++c) {
+    for (int uu = 0; uu < UPW; ++uu) {
+        const int u = u_begin + uu;
+        u32x4 wcur[F::RPU];
+#pragma unroll
+        for (int r = 0; r < F::RPU; ++r) {
+            wcur[r] = wbuf[uu % PF][r];
+            xpose4(wcur[r]);
+        }
+        // refill the ring slot with unit uu + PF
+        if (uu + PF < UPW) {
 #pragma unroll
             for (int r = 0; r < F::RPU; ++r)
-                wbuf[slot][c][r] = *(const u32x4*)(wrow[c] + (size_t)(u * F::RPU + r) * 16);
-            const size_t rowg = (size_t)ncol[c] * gpr;
-#pragma unroll
-            for (int w = 0; w < NSC; ++w) {
-                if constexpr (F::AFF) {
-                    const int grp = u * F::GPU + (F::S == 2 ? 2 * w + (j >> 1) : w);
-                    sbuf[slot][c][w] = ((const uint16_t*)a.scales)[rowg + grp];
-                    zbuf[slot][c][w] = a.biases[rowg + grp];
-                } else {
-                    const int gs = u * F::STEPS + w;
-                    const int grp = F::chunk_k(gs, j, 0) / G;
-                    sbuf[slot][c][w] = ((const uint8_t*)a.scales)[rowg + grp];
-                }
-            }
+                wbuf[uu % PF][r] = *(const u32x4*)(wrow + (size_t)((u + PF) * F::RPU + r) * 16);
         }
-    };
-
-    f32x4 acc[CB], dsum = {0.f, 0.f, 0.f, 0.f};
-    float ysum[CB][MREG];
 #pragma unroll
-    for (int c = 0; c < CB; ++c) {
-        acc[c] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < F::RPU; ++r) {
 #pragma unroll
-        for (int r = 0; r < MREG; ++r) ysum[c][r] = 0.f;
-    }
-    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-
+            for (int t = 0; t < F::SPR; ++t) {
+                const int ls = r * F::SPR + t;                 // step within unit
+                const int gs = (u * F::RPU + r) * F::SPR + t;  // global step
+                const u32x4 av = *(const u32x4*)(abase + gs * 64);
+                const bool first = F::AFF && (ls % F::WS == 0);
+                if constexpr (F::AFF) dsum = mfma_bf16(av, ones, first ? zero4 : dsum);
+                float sc = 0.f;
+                if constexpr (!F::AFF) {
+                    int byte;
+                    if constexpr (MODE == NVFP4) byte = uu * F::GPU + 2 * ls + (j >> 1);
+                    else byte = uu * F::GPU + ls;
+                    const int wd = (MODE == NVFP4) ? (uu * F::GPU + 2 * ls) / 4 : byte / 4;
+                    sc = scale_byte_to_f32<MODE>((sraw[wd] >> (8 * (byte & 3))) & 0xFFu);
+                }
+                const u32x4 bv = unpack<MODE, BITS, G>(wcur[r], t, sc);
+                acc = mfma_bf16(av, bv, first ? zero4 : acc);
+                if constexpr (F::AFF) {
+                    if (ls % F::WS == F::WS - 1) {
+                        // window done: apply the group's scale and bias
+                        const int wi = ls / F::WS;
+                        const int gw = uu * F::GPU + (F::S == 2 ? 2 * wi : wi);
+                        const int sh = (F::S == 2) ? 16 * (j >> 1) : 16 * (gw & 1);
+                        const float s = bf16_bits_to_f32((sraw[gw >> 1] >> sh) & 0xFFFFu);
+                        const float z = bf16_bits_to_f32((zraw[gw >> 1] >> sh) & 0xFFFFu);
+                        const float zz = __builtin_fmaf(-F::OFF, s, z);
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (u0 + p < u1) issue(p, u0 + p);
-
-    for (int ub = u0; ub < u1; ub += PF) {
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int u = ub + p;
-            if (u < u1) {
-#pragma unroll
-                for (int c = 0; c < CB; ++c)
-#pragma unroll
-                    for (int r = 0; r < F::RPU; ++r) xpose4(wbuf[p][c][r]);
-#pragma unroll
-                for (int r = 0; r < F::RPU; ++r) {
-#pragma unroll
-                    for (int t = 0; t < F::SPR; ++t) {
-                        const int ls = r * F::SPR + t;               // step within unit
-                        const int gs = (u * F::RPU + r) * F::SPR + t;  // global step
-                        const u32x4 av = *(const u32x4*)(abase + gs * 64);
-                        const bool first = F::AFF && (ls % F::WS == 0);
-                        if constexpr (F::AFF) {
-                            dsum = mfma_bf16(av, ones, first ? f32x4{0.f, 0.f, 0.f, 0.f} : dsum);
-                        }
-#pragma unroll
-                        for (int c = 0; c < CB; ++c) {
-                            float sc = 0.f;
-                            if constexpr (!F::AFF) sc = scale_byte_to_f32<MODE>(sbuf[p][c][ls]);
-                            const u32x4 bv = unpack<MODE, BITS, G>(wbuf[p][c][r], t, sc);
-                            acc[c] = mfma_bf16(av, bv, first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[c]);
-                        }
-                        if constexpr (F::AFF) {
-                            if (ls % F::WS == F::WS - 1) {
-                                // window done: apply the group's scale and bias
-#pragma unroll
-                                for (int c = 0; c < CB; ++c) {
-                                    const int wi = ls / F::WS;
-                                    const float s = bf16_bits_to_f32(sbuf[p][c][wi]);
-                                    const float z = bf16_bits_to_f32(zbuf[p][c][wi]);
-                                    const float zz = __builtin_fmaf(-F::OFF, s, z);
-#pragma unroll
-                                    for (int rr = 0; rr < MREG; ++rr) {
-                                        ysum[c][rr] = __builtin_fmaf(s, acc[c][rr], ysum[c][rr]);
-                                        ysum[c][rr] = __builtin_fmaf(zz, dsum[rr], ysum[c][rr]);
-                                    }
-                                }
-                            }
+                        for (int rr = 0; rr < MREG; ++rr) {
+                            ysum[rr] = __builtin_fmaf(s, acc[rr], ysum[rr]);
+                            ysum[rr] = __builtin_fmaf(zz, dsum[rr], ysum[rr]);
                         }
                     }
                 }
-                if (u + PF < u1) issue(p, u + PF);
             }
         }
     }
     if constexpr (!F::AFF) {
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-            for (int rr = 0; rr < MREG; ++rr) ysum[c][rr] = acc[c][rr];
+        for (int rr = 0; rr < MREG; ++rr) ysum[rr] = acc[rr];
     }
 
-    // ---- cross-wave reduction: red[wv][c][row][col]
+    // ---- cross-wave reduction: red[wave][row][col]
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int rr = 0; rr < MREG; ++rr) red[((wv * CB + c) * 16 + 4 * j + rr) * 16 + i] = ysum[c][rr];
+    for (int rr = 0; rr < MREG; ++rr) red[(wv * 16 + 4 * j + rr) * 16 + i] = ysum[rr];
     __syncthreads();
-    for (int o = tid; o < CB * M * 16; o += 64 * KS) {
-        const int c = o / (M * 16), rem = o - c * M * 16, m = rem / 16, col = rem & 15;
-        const int n = n0 + 16 * c + col;
+    for (int o = tid; o < M * 16; o += 64 * KS) {
+        const int m = o >> 4, col = o & 15;
+        const int n = n0 + col;
         if (n >= a.N) continue;
-        // row of MFMA output holding (slot, m)
         float v = 0.f;
         for (int w = 0; w < KS; ++w) {
             if constexpr (F::S == 2) {
-                v += red[((w * CB + c) * 16 + m) * 16 + col];
-                v += red[((w * CB + c) * 16 + 8 + m) * 16 + col];
+                v += red[(w * 16 + m) * 16 + col];
+                v += red[(w * 16 + 8 + m) * 16 + col];
             } else {
-                v += red[((w * CB + c) * 16 + m) * 16 + col];
+                v += red[(w * 16 + m) * 16 + col];
             }
         }
         a.y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_rne(v);
     }
+}
+
+// Decomposition: a wave's slice is KW = UPW units; the host picks the
+// largest power-of-two UPW (<= 8, or 4 for two-region units) dividing the
+// unit count such that the wave's x slice fits 8 chunk registers per lane
+// (M * KW <= 4096) and KS = nunits / UPW <= 16 waves.
+#ifndef QLIN_DECODE_UPW_MAX
+#define QLIN_DECODE_UPW_MAX 8   // units per wave (power of two, <= 16)
+#endif
+#ifndef QLIN_DECODE_PF
+#define QLIN_DECODE_PF 4        // weight units in flight per wave
+#endif
+
+template <int MODE, int BITS, int G>
+int pick_upw(int nunits, int M) {
+    using F = Fmt<MODE, BITS, G>;
+    int upw = F::RPU >= 2 ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
+    while (upw > 1 && (nunits % upw || M * upw * F::U > 4096)) upw >>= 1;
+    if (nunits % upw || M * upw * F::U > 4096 || nunits / upw > 16) return 0;
+    return upw;
+}
+
+template <int MODE, int BITS, int G, int UPW>
+hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
+    constexpr int PF = UPW < QLIN_DECODE_PF ? UPW : QLIN_DECODE_PF;
+    const unsigned blocks = (unsigned)((a.N + 15) / 16);
+    const unsigned threads = 64u * (unsigned)ks;
+    const size_t shm = (size_t)(a.M + 1) * xrow_bytes(a.K) + (size_t)ks * 16 * 16 * 4;
+    auto run = [&](auto kern) -> hipError_t {
+        if (shm > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            if (e != hipSuccess) return e;
+        }
+        kern<<<blocks, threads, shm, st>>>(a);
+        return hipGetLastError();
+    };
+    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1>);
+    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2>);
+    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4>);
 }
 
 template <int MODE, int BITS, int G>
@@ -358,18 +478,20 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
-    constexpr int CB = 1, KS = 4, PF = 4;
-    const unsigned blocks = (unsigned)((q.N + 16 * CB - 1) / (16 * CB));
-    const size_t shm = (size_t)(a.M + 1) * xrow_bytes(a.K) + (size_t)KS * CB * 16 * 16 * 4;
-    // rows per lane register that can hold a real output row
-    const int mreg = (F::S == 2) ? (a.M > 4 ? 4 : a.M) : (a.M > 4 ? 4 : a.M);
-    if (mreg <= 1)
-        qmm_decode_kernel<MODE, BITS, G, CB, KS, 1, PF><<<blocks, 64 * KS, shm, st>>>(a);
-    else if (mreg == 2)
-        qmm_decode_kernel<MODE, BITS, G, CB, KS, 2, PF><<<blocks, 64 * KS, shm, st>>>(a);
-    else
-        qmm_decode_kernel<MODE, BITS, G, CB, KS, 4, PF><<<blocks, 64 * KS, shm, st>>>(a);
-    return hipGetLastError();
+    const int mreg = a.M > 4 ? 4 : a.M;
+    const int nunits = a.K / F::U;
+    const int upw = pick_upw<MODE, BITS, G>(nunits, a.M);
+    if (upw == 0) return hipErrorNotSupported;
+    const int ks = nunits / upw;
+    switch (upw) {
+#if QLIN_DECODE_UPW_MAX >= 16
+    case 16: return launch_upw<MODE, BITS, G, (F::RPU >= 2 ? 8 : 16)>(a, ks, mreg, st);
+#endif
+    case 8: return launch_upw<MODE, BITS, G, 8>(a, ks, mreg, st);
+    case 4: return launch_upw<MODE, BITS, G, 4>(a, ks, mreg, st);
+    case 2: return launch_upw<MODE, BITS, G, 2>(a, ks, mreg, st);
+    default: return launch_upw<MODE, BITS, G, 1>(a, ks, mreg, st);
+    }
 }
 
 }  // namespace
@@ -382,11 +504,18 @@ bool qmm_decode_supports(const QmmArgs& q) {
     const int u = rk > q.group_size ? rk : q.group_size;
     if (q.K % u != 0) return false;
     if (q.mode == AFFINE && q.bits == 2 && q.group_size == 32 && q.M > 8) return false;
-    if (q.K > (1 << 20)) return false;
-    const size_t shm = (size_t)(q.M + 1) * xrow_bytes((int)q.K) + 4 * 16 * 16 * 4;
-    if (shm > 96 * 1024) return false;
-    // 16-byte aligned weight rows
-    if (((uintptr_t)q.wq & 15) != 0) return false;
+    // slicing rule of pick_upw(): UPW | nunits, M * UPW * U <= 4096, KS <= 16
+    const int nunits = (int)(q.K / u);
+    int upw = (u / rk >= 2) ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
+    while (upw > 1 && (nunits % upw || q.M * upw * u > 4096)) upw >>= 1;
+    if (nunits % upw || q.M * upw * u > 4096 || nunits / upw > 16) return false;
+    const size_t shm = (size_t)(q.M + 1) * xrow_bytes((int)q.K) + 16 * 16 * 16 * 4;
+    if (shm > 150 * 1024) return false;
+    // 16-byte aligned weight rows, x rows and per-wave scale blocks
+    if (((uintptr_t)q.wq & 15) != 0 || ((uintptr_t)q.x & 15) != 0) return false;
+    if (((uintptr_t)q.scales & 15) != 0 || ((uintptr_t)q.biases & 15) != 0) return false;
+    const int64_t gpr = q.K / q.group_size;
+    if ((q.mode == AFFINE ? gpr * 2 : gpr) % 16 != 0) return false;
     return true;
 }
 
