@@ -101,6 +101,8 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
     const int force = forced_path();
     if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_decode_supports(a))
         return device_status(qlin::launch_qmm_decode(a, st), "quantized_matmul (decode kernel)");
+    if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_nt_supports(a))
+        return device_status(qlin::launch_qmm_nt(a, st), "quantized_matmul ([in,out] kernel)");
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
     if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
         return device_status(qlin::launch_qmm_tiled(a, perm, offsets, st),

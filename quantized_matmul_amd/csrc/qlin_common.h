@@ -115,6 +115,9 @@ hipError_t launch_qmm_decode(const QmmArgs& a, hipStream_t s);
 hipError_t launch_qmm_tiled(const QmmArgs& a, const uint32_t* row_perm,
                             const uint32_t* expert_offsets, hipStream_t s);
 bool qmm_tiled_supports(const QmmArgs& a);
+// VALU path for the [in, out] layout (transpose = false), M <= 8, bf16 x.
+hipError_t launch_qmm_nt(const QmmArgs& a, hipStream_t s);
+bool qmm_nt_supports(const QmmArgs& a);
 bool qmm_decode_supports(const QmmArgs& a);
 // MoE bucketing: counts rows per expert, scans, and writes the stable
 // permutation of rows sorted by expert (skipped when rows are pre-sorted).

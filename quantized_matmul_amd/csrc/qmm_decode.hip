@@ -496,50 +496,79 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
 
 }  // namespace
 
-bool qmm_decode_supports(const QmmArgs& q) {
-    if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R != 0) return false;
-    if (q.M < 1 || q.M > 16 || q.N < 1) return false;
+namespace {
+
+constexpr size_t kDecodeLdsLimit = 150 * 1024;
+
+// Shape rules of the decode kernel for m activation rows (see pick_upw()).
+bool decode_shape_ok(const QmmArgs& q, int64_t m) {
     const int per = 32 / q.bits;
     const int rk = 16 * per;
     const int u = rk > q.group_size ? rk : q.group_size;
     if (q.K % u != 0) return false;
-    if (q.mode == AFFINE && q.bits == 2 && q.group_size == 32 && q.M > 8) return false;
-    // slicing rule of pick_upw(): UPW | nunits, M * UPW * U <= 4096, KS <= 16
+    if (q.mode == AFFINE && q.bits == 2 && q.group_size == 32 && m > 8) return false;
     const int nunits = (int)(q.K / u);
     int upw = (u / rk >= 2) ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
-    while (upw > 1 && (nunits % upw || q.M * upw * u > 4096)) upw >>= 1;
-    if (nunits % upw || q.M * upw * u > 4096 || nunits / upw > 16) return false;
-    const size_t shm = (size_t)(q.M + 1) * xrow_bytes((int)q.K) + 16 * 16 * 16 * 4;
-    if (shm > 150 * 1024) return false;
+    while (upw > 1 && (nunits % upw || m * upw * u > 4096)) upw >>= 1;
+    if (nunits % upw || m * upw * u > 4096 || nunits / upw > 16) return false;
+    const size_t shm = (size_t)(m + 1) * xrow_bytes((int)q.K) + 16 * 16 * 16 * 4;
+    return shm <= kDecodeLdsLimit;
+}
+
+// Largest number of activation rows one launch takes (0: none).
+int64_t decode_rows_per_pass(const QmmArgs& q) {
+    for (int64_t m = q.M < 16 ? q.M : 16; m >= 1; --m)
+        if (decode_shape_ok(q, m)) return m;
+    return 0;
+}
+
+}  // namespace
+
+bool qmm_decode_supports(const QmmArgs& q) {
+    if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R != 0) return false;
+    if (q.M < 1 || q.M > 16 || q.N < 1 || q.K > (1 << 20)) return false;
     // 16-byte aligned weight rows, x rows and per-wave scale blocks
     if (((uintptr_t)q.wq & 15) != 0 || ((uintptr_t)q.x & 15) != 0) return false;
     if (((uintptr_t)q.scales & 15) != 0 || ((uintptr_t)q.biases & 15) != 0) return false;
     const int64_t gpr = q.K / q.group_size;
     if ((q.mode == AFFINE ? gpr * 2 : gpr) % 16 != 0) return false;
-    return true;
+    // x rows that do not fit one launch's LDS run as several launches, each
+    // streaming the weight again (at most 4)
+    const int64_t rpp = decode_rows_per_pass(q);
+    return rpp > 0 && (q.M + rpp - 1) / rpp <= 4;
 }
 
-hipError_t launch_qmm_decode(const QmmArgs& q, hipStream_t st) {
-    if (!qmm_decode_supports(q)) return hipErrorNotSupported;
-    switch (q.mode) {
-    case MXFP4: return launch_fmt<MXFP4, 4, 32>(q, st);
-    case NVFP4: return launch_fmt<NVFP4, 4, 16>(q, st);
-    case MXFP8: return launch_fmt<MXFP8, 8, 32>(q, st);
-    default: break;
+hipError_t launch_qmm_decode(const QmmArgs& q0, hipStream_t st) {
+    if (!qmm_decode_supports(q0)) return hipErrorNotSupported;
+    const int64_t rpp = decode_rows_per_pass(q0);
+    for (int64_t m0 = 0; m0 < q0.M; m0 += rpp) {
+        QmmArgs q = q0;
+        q.M = (q0.M - m0) < rpp ? (q0.M - m0) : rpp;
+        q.x = (const uint16_t*)q0.x + m0 * q0.K;
+        q.y = (uint16_t*)q0.y + m0 * q0.N;
+        hipError_t e;
+        switch (q.mode) {
+        case MXFP4: e = launch_fmt<MXFP4, 4, 32>(q, st); break;
+        case NVFP4: e = launch_fmt<NVFP4, 4, 16>(q, st); break;
+        case MXFP8: e = launch_fmt<MXFP8, 8, 32>(q, st); break;
+        default:
+            if (q.bits == 4) {
+                e = q.group_size == 32 ? launch_fmt<AFFINE, 4, 32>(q, st)
+                  : q.group_size == 64 ? launch_fmt<AFFINE, 4, 64>(q, st)
+                                       : launch_fmt<AFFINE, 4, 128>(q, st);
+            } else if (q.bits == 8) {
+                e = q.group_size == 32 ? launch_fmt<AFFINE, 8, 32>(q, st)
+                  : q.group_size == 64 ? launch_fmt<AFFINE, 8, 64>(q, st)
+                                       : launch_fmt<AFFINE, 8, 128>(q, st);
+            } else {
+                e = q.group_size == 32 ? launch_fmt<AFFINE, 2, 32>(q, st)
+                  : q.group_size == 64 ? launch_fmt<AFFINE, 2, 64>(q, st)
+                                       : launch_fmt<AFFINE, 2, 128>(q, st);
+            }
+        }
+        if (e != hipSuccess) return e;
     }
-    if (q.bits == 4) {
-        if (q.group_size == 32) return launch_fmt<AFFINE, 4, 32>(q, st);
-        if (q.group_size == 64) return launch_fmt<AFFINE, 4, 64>(q, st);
-        return launch_fmt<AFFINE, 4, 128>(q, st);
-    }
-    if (q.bits == 8) {
-        if (q.group_size == 32) return launch_fmt<AFFINE, 8, 32>(q, st);
-        if (q.group_size == 64) return launch_fmt<AFFINE, 8, 64>(q, st);
-        return launch_fmt<AFFINE, 8, 128>(q, st);
-    }
-    if (q.group_size == 32) return launch_fmt<AFFINE, 2, 32>(q, st);
-    if (q.group_size == 64) return launch_fmt<AFFINE, 2, 64>(q, st);
-    return launch_fmt<AFFINE, 2, 128>(q, st);
+    return hipSuccess;
 }
 
 }  // namespace qlin

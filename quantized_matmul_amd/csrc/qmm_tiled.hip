@@ -456,7 +456,6 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
 bool qmm_tiled_supports(const QmmArgs& q) {
     if (!q.transpose || q.x_dtype != QLIN_BF16) return false;
     if (q.K % BK != 0 || q.K > (1 << 24)) return false;
-    if (q.R == 0 && q.M <= 16) return false;    // decode kernel territory
     if (q.R > 0 && (q.E > 8192 || q.R * q.M >= (1LL << 30))) return false;
     if (((uintptr_t)q.wq & 15) || ((uintptr_t)q.x & 15)) return false;
     return true;

@@ -182,6 +182,13 @@ def test_decode_kernel_micro(M, mode, g, bits):
     run_qmm_case(M, 48, 1024, bits, g, mode, "bf16", True, path="decode", wid=31)
 
 
+@pytest.mark.parametrize("M", [9, 16])
+def test_decode_kernel_row_passes(M):
+    """x rows too large for one launch's LDS run as several passes."""
+    run_qmm_case(M, 64, 8192, 4, 32, "mxfp4", "bf16", True, path="decode", wid=32)
+    run_qmm_case(M, 40, 8192, 4, 64, "affine", "bf16", True, path="decode", wid=33)
+
+
 @pytest.mark.parametrize("M,N,K", [(17, 128, 256), (100, 200, 512), (256, 256, 192), (300, 64, 256)])
 @pytest.mark.parametrize("bits,g", AFFINE_CASES)
 def test_tiled_kernel_affine(M, N, K, bits, g):
@@ -194,6 +201,20 @@ def test_tiled_kernel_affine(M, N, K, bits, g):
 @pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
 def test_tiled_kernel_micro(M, mode, g, bits):
     run_qmm_case(M, 136, 512, bits, g, mode, "bf16", True, path="tiled", wid=72)
+
+
+@pytest.mark.parametrize("M", [1, 3, 4, 8])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_nt_kernel_affine(M, bits, g):
+    """[in, out] layout (transpose=false) kernel, ragged N."""
+    run_qmm_case(M, 8 * 96 if g != 128 else 640, 512, bits, g, "affine", "bf16", False,
+                 path="decode", wid=81 + bits)
+
+
+@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_nt_kernel_micro(M, mode, g, bits):
+    run_qmm_case(M, 768, 256, bits, g, mode, "bf16", False, path="decode", wid=82)
 
 
 @pytest.mark.parametrize("transpose", [True, False])
