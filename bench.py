@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -249,7 +250,9 @@ def main():
                    "M": 1, "N": 14336, "K": 4096, "bits": 4, "group_size": 64, "mode": "affine",
                    "weight_copies_rotated": head["copies"]},
         "roofline": {"bound": "hbm", "achieved": round(head["GB/s"], 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["frac_hbm"], 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(head["frac_hbm"], 4),
+                     "traffic": profiled_traffic("qmm_decode_int4_g64_M1_N14336_K4096"),
+                     "algorithmic_bytes": head["alg_bytes"]},
         "cpu_baseline": cpu,
     }
     if pre is not None:
@@ -257,10 +260,38 @@ def main():
                            "workload": pre["workload"],
                            "roofline": {"bound": "mfma", "achieved": round(pre["TFLOP/s"], 2),
                                         "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                                        "frac": round(pre["frac_mfma"], 4), "traffic": None}}
+                                        "frac": round(pre["frac_mfma"], 4),
+                                        "traffic": profiled_traffic(
+                                            "qmm_prefill_int4_g64_M2048_N12288_K4096"),
+                                        "algorithmic_bytes": pre["alg_bytes"]}}
     line["configs"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in results]
     print(json.dumps(line), flush=True)
+
+
+def profiled_traffic(summary):
+    """HBM bytes per launch from a committed rocprofv3 counter summary.
+
+    profiles/<summary>.md carries FETCH_SIZE/WRITE_SIZE per dispatch already
+    scaled by what the same counters read for a plain device copy of known
+    size. The figure is returned only while the kernel sources hash to what
+    was profiled; a changed kernel reports null until it is profiled again.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```\n(\{.*?\})\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(seconds, log):
