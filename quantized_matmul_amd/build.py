@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_obj")
 LIB = os.path.join(HERE, "libqlin.so")
-SOURCES = ["qlin_api.cpp", "quant.hip", "qmm_generic.hip", "qmm_decode.hip", "qmm_tiled.hip", "qmm_nt.hip"]
+SOURCES = ["qlin_api.cpp", "quant.hip", "qmm_generic.hip", "qmm_decode.hip", "qmm_tiled.hip", "qmm_nt.hip",
+           "qmm_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

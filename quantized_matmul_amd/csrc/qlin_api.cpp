@@ -86,13 +86,14 @@ qlin_status check_scale_dtype(int mode, int scale_dtype, const void* biases) {
 }
 
 // Kernel path override for tests of each code path ("generic", "decode",
-// "tiled"); unset means automatic choice.
+// "tiled", "prefill"); unset means automatic choice.
 int forced_path() {
     const char* e = getenv("QLIN_FORCE_PATH");
     if (!e || !*e) return 0;
     if (!strcmp(e, "generic")) return 1;
     if (!strcmp(e, "decode")) return 2;
     if (!strcmp(e, "tiled")) return 3;
+    if (!strcmp(e, "prefill")) return 4;
     return 0;
 }
 
@@ -104,6 +105,9 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
     if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_nt_supports(a))
         return device_status(qlin::launch_qmm_nt(a, st), "quantized_matmul ([in,out] kernel)");
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
+    if (a.R == 0 && (force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
+        return device_status(qlin::launch_qmm_prefill(a, st), "quantized_matmul (prefill kernel)");
+    if (force == 4) return fail(QLIN_ERR_UNSUPPORTED, "prefill kernel does not take this shape");
     if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
         return device_status(qlin::launch_qmm_tiled(a, perm, offsets, st),
                              "quantized_matmul (tiled kernel)");

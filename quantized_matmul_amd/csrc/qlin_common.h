@@ -115,6 +115,11 @@ hipError_t launch_qmm_decode(const QmmArgs& a, hipStream_t s);
 hipError_t launch_qmm_tiled(const QmmArgs& a, const uint32_t* row_perm,
                             const uint32_t* expert_offsets, hipStream_t s);
 bool qmm_tiled_supports(const QmmArgs& a);
+// MFMA path for many rows of a plain matmul (transpose, bf16 x): the weight
+// tile is dequantized once into LDS, activations load straight into MFMA
+// operand registers.
+hipError_t launch_qmm_prefill(const QmmArgs& a, hipStream_t s);
+bool qmm_prefill_supports(const QmmArgs& a);
 // VALU path for the [in, out] layout (transpose = false), M <= 8, bf16 x.
 hipError_t launch_qmm_nt(const QmmArgs& a, hipStream_t s);
 bool qmm_nt_supports(const QmmArgs& a);

@@ -1,0 +1,428 @@
+// qmm_prefill.hip -- many-row quantized matmul on bf16 MFMA (gfx950).
+//
+// y = x . dequant(W)^T, [out, in] weight layout, bf16 activations
+// ("EMLX.Quantization", quantized_matmul; "Emily.QuantizedWeight", Layout
+// and Microscaled modes). With thousands of activation rows this is a dense
+// contraction, so the weight is dequantized once per workgroup tile and fed
+// to v_mfma_f32_16x16x32_bf16; the dense weight never reaches HBM.
+//
+// Workgroup tile: BM activation rows x BN weight rows, K in steps of 64.
+//   * Activations go from global memory straight into a three-stage LDS
+//     ring (buffer->LDS loads, no registers), two steps ahead of their use.
+//   * Packed weight codes for step k+2 are loaded into registers during step
+//     k, and dequantized during step k+1 into the other of two LDS buffers,
+//     CPC codes (one scale/bias pair) per chunk; one barrier per step.
+//   * Loads use buffer resources, so rows past the end of x or W read as
+//     zero and need no clamping or branches.
+//   * The blockIdx -> tile map keeps one row of tiles on one XCD, so the
+//     activation rows it shares stay in that XCD's L2.
+// Accumulation is fp32; lane (i, j) of an MFMA tile ends with 4 consecutive
+// output columns of one row (8-byte stores).
+
+#include "qlin_common.h"
+
+namespace qlin {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int BK = 64;              // k per step
+constexpr int LROW = BK * 2 + 16;   // LDS row pitch in bytes (16 bytes of padding)
+
+struct PrefillArgs {
+    const uint16_t* x;     // bf16 [M, K]
+    const uint32_t* wq;    // [N, K/PER]
+    const void* scales;    // [N, K/G] bf16 (affine) or u8 (microscaled)
+    const uint16_t* biases;
+    uint16_t* y;           // bf16 [M, N]
+    int M, N, K;
+};
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};  // nearest-even
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    // raw buffer (stride 0): loads at offsets >= bytes return zero. Rows past
+    // the end already have their per-lane offset past the end, so the check
+    // holds whether or not the scalar offset takes part in it.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Packed codes of one chunk: WORDS = CPC * BITS / 32 dwords.
+template <int WORDS>
+struct Chunk {
+    uint32_t w[WORDS];
+};
+
+// voff: per-lane byte offset (loop invariant); soff: wave-uniform byte
+// offset of the step. A lane whose voff is past the end reads zeros.
+template <int WORDS>
+__device__ __forceinline__ Chunk<WORDS> load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   int soff) {
+    Chunk<WORDS> c;
+    if constexpr (WORDS == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+        c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+    } else if constexpr (WORDS == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, soff, 0);
+        c.w[0] = v.x; c.w[1] = v.y;
+    } else {
+        c.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, soff, 0);
+    }
+    return c;
+}
+
+// Dequantize CPC codes (natural k order) into CPC/2 packed bf16 pairs.
+// Affine: bf16(fmaf(s, q, z)), the dequantized value rounded once to the
+// MFMA input type. Microscaled: exact decode times the group scale.
+template <int MODE, int BITS, int WORDS>
+__device__ __forceinline__ void dequant_chunk(const Chunk<WORDS>& c, float s, float z,
+                                              uint32_t* out) {
+    constexpr int PER = 32 / BITS;
+#pragma unroll
+    for (int wd = 0; wd < WORDS; ++wd) {
+        const uint32_t v = c.w[wd];
+        if constexpr (MODE == AFFINE) {
+            float f[PER];
+            if constexpr (BITS == 4) {
+                const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+                    f[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+                }
+            } else if constexpr (BITS == 8) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) f[b] = (float)((v >> (8 * b)) & 0xFFu);
+            } else {
+                const uint32_t b0 = v & 0x03030303u, b1 = (v >> 2) & 0x03030303u,
+                               b2 = (v >> 4) & 0x03030303u, b3 = (v >> 6) & 0x03030303u;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f[4 * b] = (float)((b0 >> (8 * b)) & 0xFFu);
+                    f[4 * b + 1] = (float)((b1 >> (8 * b)) & 0xFFu);
+                    f[4 * b + 2] = (float)((b2 >> (8 * b)) & 0xFFu);
+                    f[4 * b + 3] = (float)((b3 >> (8 * b)) & 0xFFu);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < PER; e += 2)
+                out[wd * PER / 2 + e / 2] =
+                    pack_bf16(__builtin_fmaf(s, f[e], z), __builtin_fmaf(s, f[e + 1], z));
+        } else if constexpr (MODE == NVFP4) {
+            out[wd * 4 + 0] = e2m1_pair_times<0>(v, s);
+            out[wd * 4 + 1] = e2m1_pair_times<1>(v, s);
+            out[wd * 4 + 2] = e2m1_pair_times<2>(v, s);
+            out[wd * 4 + 3] = e2m1_pair_times<3>(v, s);
+        } else if constexpr (BITS == 4) {  // mxfp4: the E8M0 scale is a power of two
+            out[wd * 4 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0));
+            out[wd * 4 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1));
+            out[wd * 4 + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2));
+            out[wd * 4 + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3));
+        } else {  // mxfp8
+            out[wd * 2 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, false));
+            out[wd * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, true));
+        }
+    }
+}
+
+// BM activation rows x BN weight rows per workgroup of WM x WN waves; CPC
+// codes per dequant chunk (8 or 16), chunks dealt round-robin to threads.
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC>
+__global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a) {
+    constexpr int NTH = WM * WN * 64;
+    constexpr int PER = 32 / BITS;
+    constexpr int WORDS = CPC / PER;                  // packed dwords per chunk
+    constexpr int CROW = BK / CPC;                    // chunks per weight row per step
+    constexpr int NCH = BN * CROW;                    // chunks per step
+    constexpr int CPT = (NCH + NTH - 1) / NTH;        // chunks per thread per step
+    constexpr int MW = BM / WM, NW = BN / WN;         // wave tile
+    constexpr int MT = MW / 16, NT = NW / 16;
+    static_assert(WORDS >= 1 && G % CPC == 0, "a chunk lies inside one group");
+    static_assert(MW % 16 == 0 && NW % 16 == 0, "wave tile is a multiple of the MFMA tile");
+    constexpr int NWV = WM * WN;
+    constexpr int XST = 3, XSTAGE = BM * BK * 2, WSTAGE = BN * LROW;
+    constexpr int XDMA = BM * 8 / NTH;                 // activation loads per thread per step
+    static_assert(XDMA * NTH == BM * 8, "activation tile splits into whole wave loads");
+
+    // LDS: XST activation stages [BM][128 B] (swizzled), then two
+    // dequantized weight buffers [BN][LROW]
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int i = lane & 15, j = lane >> 4;
+    const int wm = wv / WN, wn_ = wv % WN;
+
+    // tile order: blocks are dealt to the 8 XCDs round-robin; renumber so
+    // that each XCD walks a contiguous run of tiles along N
+    const int ntn = (a.N + BN - 1) / BN;
+    int b = blockIdx.x;
+    const int nblk = gridDim.x;
+    if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
+    const int m0 = (b / ntn) * BM, n0 = (b % ntn) * BN;
+
+    const uint32_t K = (uint32_t)a.K;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)a.M * K * 2u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wq, (uint32_t)a.N * (K / PER) * 4u);
+    const uint32_t ngroups = K / G;
+    constexpr uint32_t SB = MODE == AFFINE ? 2u : 1u;  // scale bytes
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, (uint32_t)a.N * ngroups * SB);
+    const __amdgpu_buffer_rsrc_t br =
+        make_rsrc(MODE == AFFINE ? (const void*)a.biases : a.scales,
+                  MODE == AFFINE ? (uint32_t)a.N * ngroups * 2u : 0u);
+
+    // ---- activation tile: XST stages in LDS, each BM rows x 128 bytes,
+    // filled by buffer->LDS loads. One wave instruction moves 8 rows (1 KB,
+    // 16 bytes per lane, lane order). Row r keeps its 16-byte chunk c in slot
+    // c ^ (r & 7), so the 16 rows an MFMA fragment reads at one k hit 8
+    // different slots (no LDS bank conflicts).
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    uint32_t xdoff[XDMA];
+#pragma unroll
+    for (int q = 0; q < XDMA; ++q) {
+        const int r = (q * NWV + wv) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        xdoff[q] = ((uint32_t)(m0 + r) * K + (uint32_t)c * 8u) * 2u;
+    }
+    auto dma_x = [&](int stage, int kt) {
+#pragma unroll
+        for (int q = 0; q < XDMA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (__attribute__((address_space(3))) void*)(smem + stage * XSTAGE + (q * NWV + wvu) * 1024),
+                16, (int)xdoff[q], kt * (BK * 2), 0, 0);
+    };
+    // fragment (s, kh) of this lane: row wm*MW + s*16 + i, chunk 4 kh + j
+    const uint32_t xfrag0 = (uint32_t)(wm * MW + i) * 128u;
+
+    // ---- dequant chunks: chunk c = tid + p*NTH -> weight row c / CROW,
+    // codes [(c % CROW) * CPC, +CPC) of the step. When the chunks do not
+    // split evenly, the spare slots reload the last chunk and skip the store.
+    uint32_t woff[CPT], goff[CPT], ldsoff[CPT];
+    bool cact[CPT];
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) {
+        int c = tid + p * NTH;
+        cact[p] = c < NCH;
+        c = c < NCH ? c : NCH - 1;
+        const int r = c / CROW, cc = c % CROW;
+        const uint32_t n = (uint32_t)(n0 + r);
+        woff[p] = (n * (K / PER) + (uint32_t)cc * WORDS) * 4u;
+        goff[p] = n * ngroups + (uint32_t)(cc * CPC) / G;   // + kt * BK / G
+        ldsoff[p] = (uint32_t)r * LROW + (uint32_t)cc * CPC * 2u;
+    }
+    // scale / bias bits stay raw until the dequant step, so nothing waits
+    // on these loads before they are needed
+    auto load_w = [&](Chunk<WORDS> (&dst)[CPT], uint32_t (&ds)[CPT], uint32_t (&dz)[CPT], int kt) {
+#pragma unroll
+        for (int p = 0; p < CPT; ++p) {
+            dst[p] = load_chunk<WORDS>(wr, woff[p], kt * (BK / PER) * 4);
+            const int gk = kt * BK / G;  // group of the step (scalar)
+            if constexpr (MODE == AFFINE) {
+                ds[p] = __builtin_amdgcn_raw_buffer_load_b16(sr, (int)(goff[p] * 2u), gk * 2, 0);
+                dz[p] = __builtin_amdgcn_raw_buffer_load_b16(br, (int)(goff[p] * 2u), gk * 2, 0);
+            } else {
+                ds[p] = __builtin_amdgcn_raw_buffer_load_b8(sr, (int)goff[p], gk, 0);
+                dz[p] = 0u;
+            }
+        }
+    };
+    auto store_w = [&](unsigned char* base, const Chunk<WORDS> (&wc)[CPT], const uint32_t (&sc)[CPT],
+                       const uint32_t (&zc)[CPT]) {
+#pragma unroll
+        for (int p = 0; p < CPT; ++p) {
+            if (NCH % NTH != 0 && !cact[p]) continue;
+            float sf, zf;
+            if constexpr (MODE == AFFINE) {
+                sf = bf16_bits_to_f32(sc[p]);
+                zf = bf16_bits_to_f32(zc[p]);
+            } else {
+                sf = MODE == NVFP4 ? e4m3_to_f32(sc[p]) : e8m0_to_f32(sc[p]);
+                zf = 0.f;
+            }
+            uint32_t o[CPC / 2];
+            dequant_chunk<MODE, BITS, WORDS>(wc[p], sf, zf, o);
+#pragma unroll
+            for (int q = 0; q < CPC / 8; ++q)
+                *(u32x4*)(base + ldsoff[p] + q * 16) = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        }
+    };
+
+    f32x4 acc[NT][MT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int s = 0; s < MT; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = a.K / BK;
+    // Register sets A and B hold packed codes for alternate steps.
+    Chunk<WORDS> wa[CPT], wb[CPT];
+    uint32_t sa[CPT], za[CPT], sb[CPT], zb[CPT];
+    unsigned char* const wbuf = smem + XST * XSTAGE;
+
+    // prologue: activations of steps 0 and 1 in flight, step 0's weights
+    // dequantized into buffer 0, step 1's codes in set A
+    dma_x(0, 0);
+    load_w(wb, sb, zb, 0);
+    dma_x(1, nk > 1 ? 1 : 0);
+    load_w(wa, sa, za, nk > 1 ? 1 : 0);
+    store_w(wbuf, wb, sb, zb);   // waits for step 0's codes, hence for its activations
+    __syncthreads();
+
+    // One step. Loads issued here land two steps later (activations) or are
+    // dequantized next step (codes). vm operations complete in order, so
+    // waiting until only this step's loads are outstanding means the
+    // activations for step kt+1 are in LDS. The step ends with that wait,
+    // lgkmcnt(0) (this wave's LDS writes done) and a plain s_barrier: a
+    // fenced barrier would also wait for this step's buffer->LDS loads.
+    constexpr int VM_PER_STEP = XDMA + CPT * (MODE == AFFINE ? 3 : 2);
+    static_assert(VM_PER_STEP < 64, "vmcnt range");
+    // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+    constexpr int WAIT_IMM = (VM_PER_STEP & 15) | (7 << 4) | (0 << 8) | ((VM_PER_STEP >> 4) << 14);
+    auto step = [&](int kt, Chunk<WORDS> (&wc)[CPT], uint32_t (&sc)[CPT], uint32_t (&zc)[CPT],
+                    Chunk<WORDS> (&wn)[CPT], uint32_t (&sn)[CPT], uint32_t (&zn)[CPT]) {
+        const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;
+        dma_x((kt + 2) % XST, k2);
+        load_w(wn, sn, zn, k2);
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char* xt = smem + (kt % XST) * XSTAGE;
+        const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            u32x4 af[NT], bf[MT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                af[t] = *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
+#pragma unroll
+            for (int s2 = 0; s2 < MT; ++s2)
+                bf[s2] = *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int s2 = 0; s2 < MT; ++s2) acc[t][s2] = mfma_bf16(af[t], bf[s2], acc[t][s2]);
+        }
+        // step kt+1's weights (beyond the last step this fills an unused buffer)
+        store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wc, sc, zc);
+        __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+        asm volatile("s_barrier" ::: "memory");
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, wa, sa, za, wb, sb, zb);
+        if (kt + 1 < nk) step(kt + 1, wb, sb, zb, wa, sa, za);
+    }
+
+    // ---- epilogue: lane holds D[n = 4j + r][m = i] of each (t, s) tile
+#pragma unroll
+    for (int s = 0; s < MT; ++s) {
+        const int m = m0 + wm * MW + s * 16 + i;
+        if (m >= a.M) continue;
+        uint16_t* yr = a.y + (size_t)m * a.N;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int n = n0 + wn_ * NW + t * 16 + 4 * j;
+            const f32x4 v = acc[t][s];
+            if (n + 3 < a.N && (a.N & 3) == 0) {
+                uint2 pk;
+                pk.x = pack_bf16(v[0], v[1]);
+                pk.y = pack_bf16(v[2], v[3]);
+                *(uint2*)(yr + n) = pk;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < a.N) yr[n + r] = (uint16_t)f32_to_bf16_rne(v[r]);
+            }
+        }
+    }
+}
+
+#ifndef QLIN_PREFILL_CFG
+#define QLIN_PREFILL_CFG 0
+#endif
+
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0>
+hipError_t launch_cfg(const PrefillArgs& t, hipStream_t st) {
+    // a chunk holds at least one packed dword
+    constexpr int CPC = CPC0 < 32 / BITS ? 32 / BITS : CPC0;
+    const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
+    auto kern = qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC>;
+    static bool attr_set = false;  // per instantiation, host side
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = ((t.M + BM - 1) / BM) * ((t.N + BN - 1) / BN);
+    kern<<<grid, WM * WN * 64, shm, st>>>(t);
+    return hipGetLastError();
+}
+
+template <int MODE, int BITS, int G>
+hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
+    PrefillArgs t{};
+    t.x = (const uint16_t*)q.x;
+    t.wq = q.wq;
+    t.scales = q.scales;
+    t.biases = (const uint16_t*)q.biases;
+    t.y = (uint16_t*)q.y;
+    t.M = (int)q.M;
+    t.N = (int)q.N;
+    t.K = (int)q.K;
+#if QLIN_PREFILL_CFG == 1
+    return launch_cfg<MODE, BITS, G, 256, 192, 2, 2, 8>(t, st);
+#elif QLIN_PREFILL_CFG == 2
+    return launch_cfg<MODE, BITS, G, 128, 384, 2, 4, 8>(t, st);
+#elif QLIN_PREFILL_CFG == 3
+    return launch_cfg<MODE, BITS, G, 256, 128, 4, 2, 8>(t, st);
+#else
+    // 8 waves (two per SIMD), 64 x 96 per wave
+    return launch_cfg<MODE, BITS, G, 256, 192, 4, 2, 8>(t, st);
+#endif
+}
+
+}  // namespace
+
+bool qmm_prefill_supports(const QmmArgs& q) {
+    if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R > 0) return false;
+    if (q.K % BK != 0 || q.M < 1) return false;
+    // 32-bit buffer offsets
+    if (q.M * q.K * 2 >= (1LL << 31) || q.N * q.K * q.bits / 8 >= (1LL << 31)) return false;
+    if (q.N * (q.K / q.group_size) * 2 >= (1LL << 31)) return false;
+    return true;
+}
+
+hipError_t launch_qmm_prefill(const QmmArgs& q, hipStream_t st) {
+    if (!qmm_prefill_supports(q)) return hipErrorNotSupported;
+    switch (q.mode) {
+    case MXFP4: return launch_fmt<MXFP4, 4, 32>(q, st);
+    case NVFP4: return launch_fmt<NVFP4, 4, 16>(q, st);
+    case MXFP8: return launch_fmt<MXFP8, 8, 32>(q, st);
+    default: break;
+    }
+    if (q.bits == 4) {
+        if (q.group_size == 32) return launch_fmt<AFFINE, 4, 32>(q, st);
+        if (q.group_size == 64) return launch_fmt<AFFINE, 4, 64>(q, st);
+        return launch_fmt<AFFINE, 4, 128>(q, st);
+    }
+    if (q.bits == 8) {
+        if (q.group_size == 32) return launch_fmt<AFFINE, 8, 32>(q, st);
+        if (q.group_size == 64) return launch_fmt<AFFINE, 8, 64>(q, st);
+        return launch_fmt<AFFINE, 8, 128>(q, st);
+    }
+    if (q.group_size == 32) return launch_fmt<AFFINE, 2, 32>(q, st);
+    if (q.group_size == 64) return launch_fmt<AFFINE, 2, 64>(q, st);
+    return launch_fmt<AFFINE, 2, 128>(q, st);
+}
+
+}  // namespace qlin

@@ -203,6 +203,22 @@ def test_tiled_kernel_micro(M, mode, g, bits):
     run_qmm_case(M, 136, 512, bits, g, mode, "bf16", True, path="tiled", wid=72)
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 128, 256), (300, 200, 512), (257, 400, 192),
+                                   (520, 385, 128), (1, 64, 64)])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_prefill_kernel_affine(M, N, K, bits, g):
+    """Many-row MFMA kernel: several tiles in both directions, ragged M and N."""
+    if K % g:
+        pytest.skip("group does not divide K")
+    run_qmm_case(M, N, K, bits, g, "affine", "bf16", True, path="prefill", wid=91 + bits)
+
+
+@pytest.mark.parametrize("M", [17, 600])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_prefill_kernel_micro(M, mode, g, bits):
+    run_qmm_case(M, 392, 512, bits, g, mode, "bf16", True, path="prefill", wid=92)
+
+
 @pytest.mark.parametrize("M", [1, 3, 4, 8])
 @pytest.mark.parametrize("bits,g", AFFINE_CASES)
 def test_nt_kernel_affine(M, bits, g):
