@@ -21,6 +21,8 @@
 
 #include "qlin_common.h"
 
+#include <stdlib.h>
+
 namespace qlin {
 namespace {
 
@@ -298,22 +300,27 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* xt = smem + (kt % XST) * XSTAGE;
         const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
+        auto mma = [&](int kh0, int kh1) {
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            u32x4 af[NT], bf[MT];
+            for (int kh = kh0; kh < kh1; ++kh) {
+                u32x4 af[NT], bf[MT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                af[t] = *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
+                for (int t = 0; t < NT; ++t)
+                    af[t] = *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
 #pragma unroll
-            for (int s2 = 0; s2 < MT; ++s2)
-                bf[s2] = *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
+                for (int s2 = 0; s2 < MT; ++s2)
+                    bf[s2] = *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int s2 = 0; s2 < MT; ++s2) acc[t][s2] = mfma_bf16(af[t], bf[s2], acc[t][s2]);
-        }
-        // step kt+1's weights (beyond the last step this fills an unused buffer)
+                    for (int s2 = 0; s2 < MT; ++s2) acc[t][s2] = mfma_bf16(af[t], bf[s2], acc[t][s2]);
+            }
+        };
+        // step kt+1's weights (beyond the last step this fills an unused
+        // buffer), dequantized between the two halves of this step's MFMAs
+        mma(0, 1);
         store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wc, sc, zc);
+        mma(1, 2);
         __builtin_amdgcn_s_waitcnt(WAIT_IMM);
         asm volatile("s_barrier" ::: "memory");
     };
@@ -346,10 +353,6 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     }
 }
 
-#ifndef QLIN_PREFILL_CFG
-#define QLIN_PREFILL_CFG 0
-#endif
-
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0>
 hipError_t launch_cfg(const PrefillArgs& t, hipStream_t st) {
     // a chunk holds at least one packed dword
@@ -368,6 +371,28 @@ hipError_t launch_cfg(const PrefillArgs& t, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Tile shapes, all 8 waves (two per SIMD): 256 x 192 (64 x 96 per wave) is
+// the most efficient per tile; 256 x 128 and 128 x 128 give more tiles when
+// the grid would not fill the chip. The choice minimises the tile area
+// times the number of rounds of 256 workgroups, with a per-shape efficiency.
+enum PrefillCfg { CFG_256x192 = 0, CFG_256x128 = 1, CFG_128x128 = 2 };
+
+int pick_cfg(int64_t M, int64_t N) {
+    const int64_t bm[3] = {256, 256, 128}, bn[3] = {192, 128, 128};
+    const double eff[3] = {1.0, 0.95, 0.75};
+    int best = 0;
+    double best_cost = 0;
+    for (int c = 0; c < 3; ++c) {
+        const int64_t tiles = ((M + bm[c] - 1) / bm[c]) * ((N + bn[c] - 1) / bn[c]);
+        const double cost = (double)((tiles + 255) / 256) * (double)(bm[c] * bn[c]) / eff[c];
+        if (c == 0 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <int MODE, int BITS, int G>
 hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     PrefillArgs t{};
@@ -379,16 +404,13 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     t.M = (int)q.M;
     t.N = (int)q.N;
     t.K = (int)q.K;
-#if QLIN_PREFILL_CFG == 1
-    return launch_cfg<MODE, BITS, G, 256, 192, 2, 2, 8>(t, st);
-#elif QLIN_PREFILL_CFG == 2
-    return launch_cfg<MODE, BITS, G, 128, 384, 2, 4, 8>(t, st);
-#elif QLIN_PREFILL_CFG == 3
-    return launch_cfg<MODE, BITS, G, 256, 128, 4, 2, 8>(t, st);
-#else
-    // 8 waves (two per SIMD), 64 x 96 per wave
-    return launch_cfg<MODE, BITS, G, 256, 192, 4, 2, 8>(t, st);
-#endif
+    int cfg = pick_cfg(q.M, q.N);
+    if (const char* e = getenv("QLIN_PREFILL_TILE")) cfg = atoi(e) % 3;  // tests of each shape
+    switch (cfg) {
+    case CFG_256x128: return launch_cfg<MODE, BITS, G, 256, 128, 4, 2, 8>(t, st);
+    case CFG_128x128: return launch_cfg<MODE, BITS, G, 128, 128, 2, 4, 8>(t, st);
+    default: return launch_cfg<MODE, BITS, G, 256, 192, 4, 2, 8>(t, st);
+    }
 }
 
 }  // namespace

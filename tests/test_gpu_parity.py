@@ -213,6 +213,17 @@ def test_prefill_kernel_affine(M, N, K, bits, g):
     run_qmm_case(M, N, K, bits, g, "affine", "bf16", True, path="prefill", wid=91 + bits)
 
 
+@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 128)])
+def test_prefill_kernel_tile_shapes(tile, bits, g):
+    """Every tile shape of the many-row kernel, forced, on ragged M and N."""
+    os.environ["QLIN_PREFILL_TILE"] = str(tile)
+    try:
+        run_qmm_case(300, 330, 256, bits, g, "affine", "bf16", True, path="prefill", wid=93)
+    finally:
+        os.environ.pop("QLIN_PREFILL_TILE", None)
+
+
 @pytest.mark.parametrize("M", [17, 600])
 @pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
 def test_prefill_kernel_micro(M, mode, g, bits):
