@@ -229,7 +229,7 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 }
 
 // Workgroup: KS waves, wave w owning K-slice [w*UPW*U, (w+1)*UPW*U) of one
-// 16-column block. A wave first issues its scale data and its slice of x
+// 16-column block. A wave first issues its slice of x and its scale data
 // (ordinary loads, before any weight), then the first PF weight units; it
 // writes its x slice into its own columns of the LDS x rows (already in
 // fragment order) and streams the remaining units through a PF-deep ring,
@@ -256,7 +256,36 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     const uint32_t* wrow = a.wq + (size_t)ncol * wpr + 4 * j;
     const size_t rowg = (size_t)ncol * gpr;
 
-    // ---- 1. scale data of the slice (contiguous in the row)
+    // ---- 1. this wave's x slice: M rows x KW elements, in blocks of BE
+    // elements (the unit of the fragment-order permutation), spread over the
+    // lanes; 16-byte chunks, at most XPL per lane
+    constexpr int BE = F::XBLOCK;                  // elements per permutation block
+    constexpr int CPB = BE / 8;                    // chunks per block
+    // chunk registers per lane: enough for the most rows this instantiation
+    // takes (host guarantees M * KW <= 4096, i.e. at most 8)
+    constexpr int MMAX = MREG == 4 ? 16 : MREG;
+    constexpr int XNEED = (MMAX * KW + 511) / 512;
+    constexpr int XPL = ((XNEED < 8 ? XNEED : 8) + CPB - 1) / CPB * CPB;
+    const int xchunks = M * (KW / 8);              // host guarantees <= 64 * XPL
+    // Buffer loads: chunks past the last row read as zero, so the loads need
+    // no branch (a branch around a load makes the compiler drain every load
+    // in flight, which would hold back the weight stream).
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x), (short)0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
+    u32x4 xr[XPL];
+#pragma unroll
+    for (int c = 0; c < XPL; ++c) {
+        // chunk id: lane-major within blocks so one lane owns whole blocks
+        const int blk = (c / CPB) * 64 + lane, part = c % CPB;
+        const int cid = blk * CPB + part;
+        const int m = cid / (KW / 8), q = cid - m * (KW / 8);
+        xr[c] = __builtin_amdgcn_raw_buffer_load_b128(
+            xrs, (int)(((uint32_t)m * (uint32_t)K + (uint32_t)(k0 + q * 8)) * 2u), 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // x first: staging it waits for nothing else
+
+    // ---- 2. scale data of the slice (contiguous in the row); after x, so
+    // that staging x waits only for x (loads complete in order)
     constexpr int SB = F::AFF ? UPW * F::GPU * 2 : UPW * F::GPU;  // bytes per slice
     constexpr int SW = (SB + 3) / 4;
     uint32_t sraw[SW], zraw[F::AFF ? SW : 1];
@@ -288,26 +317,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
         }
     }
 
-    // ---- 2. this wave's x slice: M rows x KW elements, in blocks of BE
-    // elements (the unit of the fragment-order permutation), spread over the
-    // lanes; 16-byte chunks, at most XPL per lane
-    constexpr int BE = F::XBLOCK;                  // elements per permutation block
-    constexpr int CPB = BE / 8;                    // chunks per block
-    constexpr int XPL = 8;                         // chunk registers per lane
-    const int xchunks = M * (KW / 8);              // host guarantees <= 64 * XPL
-    u32x4 xr[XPL];
-#pragma unroll
-    for (int c = 0; c < XPL; ++c) {
-        // chunk id: lane-major within blocks so one lane owns whole blocks
-        const int blk = (c / CPB) * 64 + lane, part = c % CPB;
-        const int cid = blk * CPB + part;
-        xr[c] = u32x4{0u, 0u, 0u, 0u};
-        if (cid < xchunks) {
-            const int m = cid / (KW / 8), q = cid - m * (KW / 8);
-            xr[c] = *(const u32x4*)(a.x + (size_t)m * K + k0 + q * 8);
-        }
-    }
-
+    __builtin_amdgcn_sched_barrier(0);
     // ---- 3. the first PF weight units
     u32x4 wbuf[PF][F::RPU];
 #pragma unroll
