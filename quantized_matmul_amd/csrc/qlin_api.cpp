@@ -105,8 +105,9 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
     if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_nt_supports(a))
         return device_status(qlin::launch_qmm_nt(a, st), "quantized_matmul ([in,out] kernel)");
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
-    if (a.R == 0 && (force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
-        return device_status(qlin::launch_qmm_prefill(a, st), "quantized_matmul (prefill kernel)");
+    if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
+        return device_status(qlin::launch_qmm_prefill(a, perm, offsets, st),
+                             a.R ? "gather_qmm (many-row kernel)" : "quantized_matmul (prefill kernel)");
     if (force == 4) return fail(QLIN_ERR_UNSUPPORTED, "prefill kernel does not take this shape");
     if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
         return device_status(qlin::launch_qmm_tiled(a, perm, offsets, st),
@@ -252,9 +253,11 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
     a.rhs = rhs_indices;
     hipStream_t s = (hipStream_t)stream;
     uint32_t *perm = nullptr, *offsets = nullptr;
-    if (qlin::qmm_tiled_supports(a) && forced_path() != 1) {
-        hipError_t e = qlin::launch_bucket(rhs_indices, R, E, M, sorted_indices, workspace, &perm,
-                                           &offsets, s);
+    // bucketing serves both MFMA paths (they tile rows alike)
+    static_assert(qlin::kPrefillGatherRows == 64, "bucket tiles shared by the MFMA gather paths");
+    if ((qlin::qmm_prefill_supports(a) || qlin::qmm_tiled_supports(a)) && forced_path() != 1) {
+        hipError_t e = qlin::launch_bucket(rhs_indices, R, E, M, sorted_indices,
+                                           qlin::kPrefillGatherRows, workspace, &perm, &offsets, s);
         if (e != hipSuccess) return device_status(e, "gather_qmm (expert bucketing)");
     }
     return run_qmm(a, perm, offsets, s);

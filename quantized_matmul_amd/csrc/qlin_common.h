@@ -115,10 +115,12 @@ hipError_t launch_qmm_decode(const QmmArgs& a, hipStream_t s);
 hipError_t launch_qmm_tiled(const QmmArgs& a, const uint32_t* row_perm,
                             const uint32_t* expert_offsets, hipStream_t s);
 bool qmm_tiled_supports(const QmmArgs& a);
-// MFMA path for many rows of a plain matmul (transpose, bf16 x): the weight
-// tile is dequantized once into LDS, activations load straight into MFMA
-// operand registers.
-hipError_t launch_qmm_prefill(const QmmArgs& a, hipStream_t s);
+// MFMA path for many rows (transpose, bf16 x), plain or expert-gathered:
+// the weight tile is dequantized once into LDS per tile of activation rows.
+// The gather form needs the bucketing below, run with kPrefillGatherRows.
+constexpr int kPrefillGatherRows = 64;
+hipError_t launch_qmm_prefill(const QmmArgs& a, const uint32_t* row_perm,
+                              const uint32_t* expert_offsets, hipStream_t s);
 bool qmm_prefill_supports(const QmmArgs& a);
 // VALU path for the [in, out] layout (transpose = false), M <= 8, bf16 x.
 hipError_t launch_qmm_nt(const QmmArgs& a, hipStream_t s);
@@ -126,9 +128,10 @@ bool qmm_nt_supports(const QmmArgs& a);
 bool qmm_decode_supports(const QmmArgs& a);
 // MoE bucketing: counts rows per expert, scans, and writes the stable
 // permutation of rows sorted by expert (skipped when rows are pre-sorted).
+// rows_per_tile sets the row-tile prefix written after the offsets.
 hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, int sorted,
-                         void* workspace, uint32_t** row_perm, uint32_t** expert_offsets,
-                         hipStream_t s);
+                         int rows_per_tile, void* workspace, uint32_t** row_perm,
+                         uint32_t** expert_offsets, hipStream_t s);
 size_t bucket_workspace_bytes(int64_t R, int64_t E);
 
 }  // namespace qlin

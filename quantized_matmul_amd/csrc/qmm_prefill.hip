@@ -36,12 +36,18 @@ constexpr int BK = 64;              // k per step
 constexpr int LROW = BK * 2 + 16;   // LDS row pitch in bytes (16 bytes of padding)
 
 struct PrefillArgs {
-    const uint16_t* x;     // bf16 [M, K]
-    const uint32_t* wq;    // [N, K/PER]
-    const void* scales;    // [N, K/G] bf16 (affine) or u8 (microscaled)
+    const uint16_t* x;     // bf16 [M, K]; gather: [B, M, K]
+    const uint32_t* wq;    // [N, K/PER]; gather: [E][N][K/PER]
+    const void* scales;    // [N, K/G] bf16 (affine) or u8 (microscaled); gather: per expert
     const uint16_t* biases;
-    uint16_t* y;           // bf16 [M, N]
-    int M, N, K;
+    uint16_t* y;           // bf16 [M, N]; gather: [R, M, N]
+    int M, N, K;           // gather: M = activation rows per index row
+    // gather form (expert-bucketed rows)
+    const uint32_t* lhs;      // [R] or null (identity)
+    const uint32_t* perm;     // [R] index rows in expert order
+    const uint32_t* offsets;  // [E+1] index-row offset of each expert
+    const uint32_t* tiles;    // [E+1] row-tile prefix of each expert
+    int E, B;
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -142,7 +148,7 @@ __device__ __forceinline__ void dequant_chunk(const Chunk<WORDS>& c, float s, fl
 
 // BM activation rows x BN weight rows per workgroup of WM x WN waves; CPC
 // codes per dequant chunk (8 or 16), chunks dealt round-robin to threads.
-template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC>
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC, bool GATHER>
 __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a) {
     constexpr int NTH = WM * WN * 64;
     constexpr int PER = 32 / BITS;
@@ -167,23 +173,61 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     const int i = lane & 15, j = lane >> 4;
     const int wm = wv / WN, wn_ = wv % WN;
 
-    // tile order: blocks are dealt to the 8 XCDs round-robin; renumber so
-    // that each XCD walks a contiguous run of tiles along N
     const int ntn = (a.N + BN - 1) / BN;
-    int b = blockIdx.x;
-    const int nblk = gridDim.x;
-    if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
-    const int m0 = (b / ntn) * BM, n0 = (b % ntn) * BN;
+    int m0, n0;
+    int expert = 0, row_begin = 0, row_count = a.M;   // GEMM rows of this tile's problem
+    if constexpr (GATHER) {
+        // (expert, row tile, column tile): the grid holds an upper bound on
+        // the row tiles; tiles past the real count leave at once
+        int tile_m = blockIdx.x / ntn;
+        n0 = (blockIdx.x % ntn) * BN;
+        if (tile_m >= (int)a.tiles[a.E]) return;
+        int lo = 0, hi = a.E;                     // tiles[lo] <= tile_m < tiles[lo + 1]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)a.tiles[mid] <= tile_m) lo = mid; else hi = mid;
+        }
+        expert = lo;
+        m0 = (tile_m - (int)a.tiles[lo]) * BM;
+        row_begin = (int)a.offsets[lo];
+        row_count = ((int)a.offsets[lo + 1] - row_begin) * a.M;
+    } else {
+        // blocks are dealt to the 8 XCDs round-robin; renumber so that each
+        // XCD walks a contiguous run of tiles along N
+        int b = blockIdx.x;
+        const int nblk = gridDim.x;
+        if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
+        m0 = (b / ntn) * BM;
+        n0 = (b % ntn) * BN;
+    }
+    // GEMM row rho of the tile's problem -> index row (gather) / x row / y row
+    auto x_row = [&](int rho) -> uint32_t {
+        if constexpr (GATHER) {
+            const uint32_t ir = a.perm[row_begin + rho / a.M];
+            const uint32_t bx = a.lhs ? a.lhs[ir] : ir;
+            return bx * (uint32_t)a.M + (uint32_t)(rho % a.M);
+        } else {
+            return (uint32_t)rho;
+        }
+    };
+    auto y_row = [&](int rho) -> size_t {
+        if constexpr (GATHER)
+            return (size_t)a.perm[row_begin + rho / a.M] * a.M + (size_t)(rho % a.M);
+        else
+            return (size_t)rho;
+    };
 
     const uint32_t K = (uint32_t)a.K;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)a.M * K * 2u);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wq, (uint32_t)a.N * (K / PER) * 4u);
+    const uint32_t xrows = GATHER ? (uint32_t)a.B * (uint32_t)a.M : (uint32_t)a.M;
+    const uint32_t nrows = (uint32_t)(GATHER ? a.E : 1) * (uint32_t)a.N;  // stacked weight rows
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, xrows * K * 2u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wq, nrows * (K / PER) * 4u);
     const uint32_t ngroups = K / G;
     constexpr uint32_t SB = MODE == AFFINE ? 2u : 1u;  // scale bytes
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, (uint32_t)a.N * ngroups * SB);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, nrows * ngroups * SB);
     const __amdgpu_buffer_rsrc_t br =
         make_rsrc(MODE == AFFINE ? (const void*)a.biases : a.scales,
-                  MODE == AFFINE ? (uint32_t)a.N * ngroups * 2u : 0u);
+                  MODE == AFFINE ? nrows * ngroups * 2u : 0u);
 
     // ---- activation tile: XST stages in LDS, each BM rows x 128 bytes,
     // filled by buffer->LDS loads. One wave instruction moves 8 rows (1 KB,
@@ -196,7 +240,8 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     for (int q = 0; q < XDMA; ++q) {
         const int r = (q * NWV + wv) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
-        xdoff[q] = ((uint32_t)(m0 + r) * K + (uint32_t)c * 8u) * 2u;
+        // rows past the problem read zeros: their offset is past the buffer
+        xdoff[q] = m0 + r < row_count ? (x_row(m0 + r) * K + (uint32_t)c * 8u) * 2u : 0x80000000u;
     }
     auto dma_x = [&](int stage, int kt) {
 #pragma unroll
@@ -219,7 +264,9 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         cact[p] = c < NCH;
         c = c < NCH ? c : NCH - 1;
         const int r = c / CROW, cc = c % CROW;
-        const uint32_t n = (uint32_t)(n0 + r);
+        // rows past N read the next expert's rows (or zeros past the end);
+        // their outputs are never stored
+        const uint32_t n = (uint32_t)expert * (uint32_t)a.N + (uint32_t)(n0 + r);
         woff[p] = (n * (K / PER) + (uint32_t)cc * WORDS) * 4u;
         goff[p] = n * ngroups + (uint32_t)(cc * CPC) / G;   // + kt * BK / G
         ldsoff[p] = (uint32_t)r * LROW + (uint32_t)cc * CPC * 2u;
@@ -333,8 +380,8 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
 #pragma unroll
     for (int s = 0; s < MT; ++s) {
         const int m = m0 + wm * MW + s * 16 + i;
-        if (m >= a.M) continue;
-        uint16_t* yr = a.y + (size_t)m * a.N;
+        if (m >= row_count) continue;
+        uint16_t* yr = a.y + y_row(m) * a.N;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int n = n0 + wn_ * NW + t * 16 + 4 * j;
@@ -353,12 +400,12 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     }
 }
 
-template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0>
-hipError_t launch_cfg(const PrefillArgs& t, hipStream_t st) {
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, bool GATHER>
+hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     // a chunk holds at least one packed dword
     constexpr int CPC = CPC0 < 32 / BITS ? 32 / BITS : CPC0;
     const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
-    auto kern = qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC>;
+    auto kern = qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER>;
     static bool attr_set = false;  // per instantiation, host side
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -366,9 +413,14 @@ hipError_t launch_cfg(const PrefillArgs& t, hipStream_t st) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int grid = ((t.M + BM - 1) / BM) * ((t.N + BN - 1) / BN);
     kern<<<grid, WM * WN * 64, shm, st>>>(t);
     return hipGetLastError();
+}
+
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0>
+hipError_t launch_plain(const PrefillArgs& t, hipStream_t st) {
+    const int grid = ((t.M + BM - 1) / BM) * ((t.N + BN - 1) / BN);
+    return launch_cfg<MODE, BITS, G, BM, BN, WM, WN, CPC0, false>(t, grid, st);
 }
 
 // Tile shapes, all 8 waves (two per SIMD): 256 x 192 (64 x 96 per wave) is
@@ -407,44 +459,96 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     int cfg = pick_cfg(q.M, q.N);
     if (const char* e = getenv("QLIN_PREFILL_TILE")) cfg = atoi(e) % 3;  // tests of each shape
     switch (cfg) {
-    case CFG_256x128: return launch_cfg<MODE, BITS, G, 256, 128, 4, 2, 8>(t, st);
-    case CFG_128x128: return launch_cfg<MODE, BITS, G, 128, 128, 2, 4, 8>(t, st);
-    default: return launch_cfg<MODE, BITS, G, 256, 192, 4, 2, 8>(t, st);
+    case CFG_256x128: return launch_plain<MODE, BITS, G, 256, 128, 4, 2, 8>(t, st);
+    case CFG_128x128: return launch_plain<MODE, BITS, G, 128, 128, 2, 4, 8>(t, st);
+    default: return launch_plain<MODE, BITS, G, 256, 192, 4, 2, 8>(t, st);
     }
+}
+
+// Expert-bucketed rows: BM = 64 rows of one expert (a typical expert's share
+// of a token batch), 192 weight rows, 32 x 48 per wave.
+template <int MODE, int BITS, int G>
+hipError_t launch_gather_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,
+                             hipStream_t st) {
+    PrefillArgs t{};
+    t.x = (const uint16_t*)q.x;
+    t.wq = q.wq;
+    t.scales = q.scales;
+    t.biases = (const uint16_t*)q.biases;
+    t.y = (uint16_t*)q.y;
+    t.M = (int)q.M;
+    t.N = (int)q.N;
+    t.K = (int)q.K;
+    t.lhs = q.lhs;
+    t.perm = perm;
+    t.offsets = offsets;
+    t.tiles = offsets + (q.E + 1);
+    t.E = (int)q.E;
+    t.B = (int)q.batch_x;
+    constexpr int BM = kPrefillGatherRows, BN = 192;
+    // upper bound on row tiles: every expert may add one partial tile
+    const int64_t mt = (q.R * q.M + BM - 1) / BM + q.E;
+    const int grid = (int)(mt * ((q.N + BN - 1) / BN));
+    return launch_cfg<MODE, BITS, G, BM, BN, 2, 4, 8, true>(t, grid, st);
+}
+
+}  // namespace
+
+namespace {
+
+template <int MODE, int BITS, int G>
+struct FmtTag {};
+
+// Calls fn(FmtTag<mode, bits, group>{}) for the (mode, bits, group) of q.
+template <class Fn>
+hipError_t dispatch_fmt(const QmmArgs& q, Fn&& fn) {
+    switch (q.mode) {
+    case MXFP4: return fn(FmtTag<MXFP4, 4, 32>{});
+    case NVFP4: return fn(FmtTag<NVFP4, 4, 16>{});
+    case MXFP8: return fn(FmtTag<MXFP8, 8, 32>{});
+    default: break;
+    }
+    if (q.bits == 4) {
+        if (q.group_size == 32) return fn(FmtTag<AFFINE, 4, 32>{});
+        if (q.group_size == 64) return fn(FmtTag<AFFINE, 4, 64>{});
+        return fn(FmtTag<AFFINE, 4, 128>{});
+    }
+    if (q.bits == 8) {
+        if (q.group_size == 32) return fn(FmtTag<AFFINE, 8, 32>{});
+        if (q.group_size == 64) return fn(FmtTag<AFFINE, 8, 64>{});
+        return fn(FmtTag<AFFINE, 8, 128>{});
+    }
+    if (q.group_size == 32) return fn(FmtTag<AFFINE, 2, 32>{});
+    if (q.group_size == 64) return fn(FmtTag<AFFINE, 2, 64>{});
+    return fn(FmtTag<AFFINE, 2, 128>{});
+}
+
+template <int MODE, int BITS, int G>
+hipError_t launch_tag(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,
+                      hipStream_t st, FmtTag<MODE, BITS, G>) {
+    if (q.R > 0) return launch_gather_fmt<MODE, BITS, G>(q, perm, offsets, st);
+    return launch_fmt<MODE, BITS, G>(q, st);
 }
 
 }  // namespace
 
 bool qmm_prefill_supports(const QmmArgs& q) {
-    if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R > 0) return false;
+    if (!q.transpose || q.x_dtype != QLIN_BF16) return false;
     if (q.K % BK != 0 || q.M < 1) return false;
-    // 32-bit buffer offsets
-    if (q.M * q.K * 2 >= (1LL << 31) || q.N * q.K * q.bits / 8 >= (1LL << 31)) return false;
-    if (q.N * (q.K / q.group_size) * 2 >= (1LL << 31)) return false;
+    if (q.R > 0 && (q.E > 8192 || q.R * q.M >= (1LL << 30))) return false;
+    // 32-bit buffer offsets over x, the (stacked) weight and its scales
+    const int64_t xrows = q.R > 0 ? q.batch_x * q.M : q.M;
+    const int64_t wrows = (q.R > 0 ? q.E : 1) * q.N;
+    if (xrows * q.K * 2 >= (1LL << 31) || wrows * q.K * q.bits / 8 >= (1LL << 31)) return false;
+    if (wrows * (q.K / q.group_size) * 2 >= (1LL << 31)) return false;
     return true;
 }
 
-hipError_t launch_qmm_prefill(const QmmArgs& q, hipStream_t st) {
+hipError_t launch_qmm_prefill(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,
+                              hipStream_t st) {
     if (!qmm_prefill_supports(q)) return hipErrorNotSupported;
-    switch (q.mode) {
-    case MXFP4: return launch_fmt<MXFP4, 4, 32>(q, st);
-    case NVFP4: return launch_fmt<NVFP4, 4, 16>(q, st);
-    case MXFP8: return launch_fmt<MXFP8, 8, 32>(q, st);
-    default: break;
-    }
-    if (q.bits == 4) {
-        if (q.group_size == 32) return launch_fmt<AFFINE, 4, 32>(q, st);
-        if (q.group_size == 64) return launch_fmt<AFFINE, 4, 64>(q, st);
-        return launch_fmt<AFFINE, 4, 128>(q, st);
-    }
-    if (q.bits == 8) {
-        if (q.group_size == 32) return launch_fmt<AFFINE, 8, 32>(q, st);
-        if (q.group_size == 64) return launch_fmt<AFFINE, 8, 64>(q, st);
-        return launch_fmt<AFFINE, 8, 128>(q, st);
-    }
-    if (q.group_size == 32) return launch_fmt<AFFINE, 2, 32>(q, st);
-    if (q.group_size == 64) return launch_fmt<AFFINE, 2, 64>(q, st);
-    return launch_fmt<AFFINE, 2, 128>(q, st);
+    if (q.R > 0 && (!perm || !offsets)) return hipErrorInvalidValue;
+    return dispatch_fmt(q, [&](auto tag) { return launch_tag(q, perm, offsets, st, tag); });
 }
 
 }  // namespace qlin

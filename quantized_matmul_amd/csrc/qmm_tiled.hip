@@ -467,13 +467,15 @@ size_t bucket_workspace_bytes(int64_t R, int64_t E) {
 }
 
 hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, int sorted,
-                         void* workspace, uint32_t** perm, uint32_t** offsets, hipStream_t st) {
+                         int rows_per_tile, void* workspace, uint32_t** perm, uint32_t** offsets,
+                         hipStream_t st) {
     uint32_t* ws = (uint32_t*)workspace;
     *offsets = ws;                   // [E+1] then tiles [E+1]
     *perm = ws + 2 * (E + 1);
     const size_t shm = (size_t)2 * E * sizeof(uint32_t);
     if (shm > 64 * 1024) return hipErrorInvalidValue;
-    bucket_kernel<<<1, 1024, shm, st>>>(rhs, (int)R, (int)E, (int)M, GATHER_BM, sorted, *offsets,
+    if (rows_per_tile != GATHER_BM) return hipErrorInvalidValue;  // tiles for this kernel's BM
+    bucket_kernel<<<1, 1024, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted, *offsets,
                                         *offsets + (E + 1), *perm);
     return hipGetLastError();
 }

@@ -352,22 +352,25 @@ def test_gather_identity_lhs_and_micro():
     run_gather_case(6, 2, 256, 64, 4, [1, 1, 0, 3, 2, 0], None, transpose=False, wid=66)
 
 
+@pytest.mark.parametrize("path", ["tiled", "prefill"])
 @pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8)] + MICRO_CASES)
-def test_gather_tiled_modes(mode, g, bits):
+def test_gather_mfma_modes(mode, g, bits, path):
+    """Both MFMA gather kernels; M = 3 rows per index row, ragged N = 200."""
     T, E, k = 40, 6, 2
     rhs = synth.topk_distinct(T, E, k, 68)
     lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
-    run_gather_case(T, 3, 256, 200, E, rhs, lhs, bits=bits, g=g, mode=mode, wid=68)
+    run_gather_case(T, 3, 256, 200, E, rhs, lhs, bits=bits, g=g, mode=mode, path=path, wid=68)
 
 
-def test_gather_skewed_experts():
+@pytest.mark.parametrize("path", ["tiled", "prefill"])
+def test_gather_skewed_experts(path):
     """One hot expert with 150 rows (several row tiles), several empty ones."""
     rhs = np.array([5] * 150 + [0] * 3 + [2] * 70, np.uint32)
     np.random.default_rng(3).shuffle(rhs)
-    run_gather_case(rhs.size, 1, 128, 96, 9, rhs, None, wid=69)
+    run_gather_case(rhs.size, 1, 128, 96, 9, rhs, None, path=path, wid=69)
     order = np.argsort(rhs, kind="stable")
     run_gather_case(rhs.size, 1, 128, 96, 9, rhs[order], order.astype(np.uint32),
-                    sorted_indices=True, wid=69)
+                    sorted_indices=True, path=path, wid=69)
 
 
 def test_gather_sorted_flag_is_only_a_hint():
