@@ -253,11 +253,16 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
     a.rhs = rhs_indices;
     hipStream_t s = (hipStream_t)stream;
     uint32_t *perm = nullptr, *offsets = nullptr;
-    // bucketing serves both MFMA paths (they tile rows alike)
-    static_assert(qlin::kPrefillGatherRows == 64, "bucket tiles shared by the MFMA gather paths");
-    if ((qlin::qmm_prefill_supports(a) || qlin::qmm_tiled_supports(a)) && forced_path() != 1) {
-        hipError_t e = qlin::launch_bucket(rhs_indices, R, E, M, sorted_indices,
-                                           qlin::kPrefillGatherRows, workspace, &perm, &offsets, s);
+    // the MFMA paths read rows bucketed by expert, in tiles of their own size
+    const int force = forced_path();
+    int tile_rows = 0;
+    if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
+        tile_rows = qlin::kPrefillGatherRows;
+    else if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
+        tile_rows = qlin::kTiledGatherRows;
+    if (tile_rows) {
+        hipError_t e = qlin::launch_bucket(rhs_indices, R, E, M, sorted_indices, tile_rows,
+                                           workspace, &perm, &offsets, s);
         if (e != hipSuccess) return device_status(e, "gather_qmm (expert bucketing)");
     }
     return run_qmm(a, perm, offsets, s);

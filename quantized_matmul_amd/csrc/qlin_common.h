@@ -118,7 +118,11 @@ bool qmm_tiled_supports(const QmmArgs& a);
 // MFMA path for many rows (transpose, bf16 x), plain or expert-gathered:
 // the weight tile is dequantized once into LDS per tile of activation rows.
 // The gather form needs the bucketing below, run with kPrefillGatherRows.
-constexpr int kPrefillGatherRows = 64;
+#ifndef QLIN_PREFILL_GATHER_ROWS
+#define QLIN_PREFILL_GATHER_ROWS 64
+#endif
+constexpr int kPrefillGatherRows = QLIN_PREFILL_GATHER_ROWS;
+constexpr int kTiledGatherRows = 64;   // row tile of the LDS-tiled gather kernel
 hipError_t launch_qmm_prefill(const QmmArgs& a, const uint32_t* row_perm,
                               const uint32_t* expert_offsets, hipStream_t s);
 bool qmm_prefill_supports(const QmmArgs& a);

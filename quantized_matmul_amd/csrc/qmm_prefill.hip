@@ -23,6 +23,8 @@
 
 #include <stdlib.h>
 
+#include <type_traits>
+
 namespace qlin {
 namespace {
 
@@ -68,6 +70,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                              0x00020000);
 }
 
+// f(integral_constant<int, U>) for U = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        unroll<B + 1, E>(f);
+    }
+}
+
 // Packed codes of one chunk: WORDS = CPC * BITS / 32 dwords.
 template <int WORDS>
 struct Chunk {
@@ -80,7 +91,12 @@ template <int WORDS>
 __device__ __forceinline__ Chunk<WORDS> load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                    int soff) {
     Chunk<WORDS> c;
-    if constexpr (WORDS == 4) {
+    if constexpr (WORDS == 8) {
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff + 16, soff, 0);
+        c.w[0] = v0.x; c.w[1] = v0.y; c.w[2] = v0.z; c.w[3] = v0.w;
+        c.w[4] = v1.x; c.w[5] = v1.y; c.w[6] = v1.z; c.w[7] = v1.w;
+    } else if constexpr (WORDS == 4) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
         c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
     } else if constexpr (WORDS == 2) {
@@ -148,14 +164,19 @@ __device__ __forceinline__ void dequant_chunk(const Chunk<WORDS>& c, float s, fl
 
 // BM activation rows x BN weight rows per workgroup of WM x WN waves; CPC
 // codes per dequant chunk (8 or 16), chunks dealt round-robin to threads.
-template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC, bool GATHER>
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC, bool GATHER, int WPF>
 __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a) {
     constexpr int NTH = WM * WN * 64;
     constexpr int PER = 32 / BITS;
     constexpr int WORDS = CPC / PER;                  // packed dwords per chunk
     constexpr int CROW = BK / CPC;                    // chunks per weight row per step
     constexpr int NCH = BN * CROW;                    // chunks per step
-    constexpr int CPT = (NCH + NTH - 1) / NTH;        // chunks per thread per step
+    // run length: chunks of one row a thread dequantizes per step
+    constexpr int RCH = (NCH % NTH == 0 && NCH / NTH <= CROW && CROW % (NCH / NTH) == 0) ? NCH / NTH : 1;
+    constexpr int CPT = RCH > 1 ? 1 : (NCH + NTH - 1) / NTH;   // runs (or chunks) per thread
+    constexpr int RWORDS = RCH * WORDS;               // packed dwords per run
+    constexpr int NGT = (RCH * CPC + G - 1) / G;      // groups a run spans (1 or 2)
+    static_assert(NGT <= 2 && (NGT == 1 || RCH * CPC == 2 * G), "a run spans one or two whole groups");
     constexpr int MW = BM / WM, NW = BN / WN;         // wave tile
     constexpr int MT = MW / 16, NT = NW / 16;
     static_assert(WORDS >= 1 && G % CPC == 0, "a chunk lies inside one group");
@@ -253,17 +274,27 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     // fragment (s, kh) of this lane: row wm*MW + s*16 + i, chunk 4 kh + j
     const uint32_t xfrag0 = (uint32_t)(wm * MW + i) * 128u;
 
-    // ---- dequant chunks: chunk c = tid + p*NTH -> weight row c / CROW,
-    // codes [(c % CROW) * CPC, +CPC) of the step. When the chunks do not
-    // split evenly, the spare slots reload the last chunk and skip the store.
+    // ---- dequant work. With runs (RCH > 1) a thread owns RCH consecutive
+    // chunks of one weight row per step: one load of RCH*CPC codes and one
+    // scale (and bias) load of the groups they span. Otherwise chunk
+    // c = tid + p*NTH -> weight row c / CROW, chunk c % CROW; spare slots of an
+    // uneven split reload the last chunk and skip the store.
     uint32_t woff[CPT], goff[CPT], ldsoff[CPT];
     bool cact[CPT];
 #pragma unroll
     for (int p = 0; p < CPT; ++p) {
-        int c = tid + p * NTH;
-        cact[p] = c < NCH;
-        c = c < NCH ? c : NCH - 1;
-        const int r = c / CROW, cc = c % CROW;
+        int r, cc;
+        if constexpr (RCH > 1) {
+            r = tid / (CROW / RCH);
+            cc = (tid % (CROW / RCH)) * RCH;
+            cact[p] = true;
+        } else {
+            int c = tid + p * NTH;
+            cact[p] = c < NCH;
+            c = c < NCH ? c : NCH - 1;
+            r = c / CROW;
+            cc = c % CROW;
+        }
         // rows past N read the next expert's rows (or zeros past the end);
         // their outputs are never stored
         const uint32_t n = (uint32_t)expert * (uint32_t)a.N + (uint32_t)(n0 + r);
@@ -273,38 +304,58 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     }
     // scale / bias bits stay raw until the dequant step, so nothing waits
     // on these loads before they are needed
-    auto load_w = [&](Chunk<WORDS> (&dst)[CPT], uint32_t (&ds)[CPT], uint32_t (&dz)[CPT], int kt) {
+    auto load_w = [&](Chunk<RWORDS> (&dst)[CPT], uint32_t (&ds)[CPT], uint32_t (&dz)[CPT], int kt) {
 #pragma unroll
         for (int p = 0; p < CPT; ++p) {
-            dst[p] = load_chunk<WORDS>(wr, woff[p], kt * (BK / PER) * 4);
+            dst[p] = load_chunk<RWORDS>(wr, woff[p], kt * (BK / PER) * 4);
             const int gk = kt * BK / G;  // group of the step (scalar)
             if constexpr (MODE == AFFINE) {
-                ds[p] = __builtin_amdgcn_raw_buffer_load_b16(sr, (int)(goff[p] * 2u), gk * 2, 0);
-                dz[p] = __builtin_amdgcn_raw_buffer_load_b16(br, (int)(goff[p] * 2u), gk * 2, 0);
+                // one 2-byte value per group spanned (NGT = 1 or 2)
+                if constexpr (NGT == 1) {
+                    ds[p] = __builtin_amdgcn_raw_buffer_load_b16(sr, (int)(goff[p] * 2u), gk * 2, 0);
+                    dz[p] = __builtin_amdgcn_raw_buffer_load_b16(br, (int)(goff[p] * 2u), gk * 2, 0);
+                } else {
+                    ds[p] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)(goff[p] * 2u), gk * 2, 0);
+                    dz[p] = __builtin_amdgcn_raw_buffer_load_b32(br, (int)(goff[p] * 2u), gk * 2, 0);
+                }
             } else {
-                ds[p] = __builtin_amdgcn_raw_buffer_load_b8(sr, (int)goff[p], gk, 0);
+                if constexpr (NGT == 1)
+                    ds[p] = __builtin_amdgcn_raw_buffer_load_b8(sr, (int)goff[p], gk, 0);
+                else
+                    ds[p] = __builtin_amdgcn_raw_buffer_load_b16(sr, (int)goff[p], gk, 0);
                 dz[p] = 0u;
             }
         }
     };
-    auto store_w = [&](unsigned char* base, const Chunk<WORDS> (&wc)[CPT], const uint32_t (&sc)[CPT],
+    auto store_w = [&](unsigned char* base, const Chunk<RWORDS> (&wc)[CPT], const uint32_t (&sc)[CPT],
                        const uint32_t (&zc)[CPT]) {
 #pragma unroll
         for (int p = 0; p < CPT; ++p) {
-            if (NCH % NTH != 0 && !cact[p]) continue;
-            float sf, zf;
-            if constexpr (MODE == AFFINE) {
-                sf = bf16_bits_to_f32(sc[p]);
-                zf = bf16_bits_to_f32(zc[p]);
-            } else {
-                sf = MODE == NVFP4 ? e4m3_to_f32(sc[p]) : e8m0_to_f32(sc[p]);
-                zf = 0.f;
-            }
-            uint32_t o[CPC / 2];
-            dequant_chunk<MODE, BITS, WORDS>(wc[p], sf, zf, o);
+            if (RCH == 1 && NCH % NTH != 0 && !cact[p]) continue;
 #pragma unroll
-            for (int q = 0; q < CPC / 8; ++q)
-                *(u32x4*)(base + ldsoff[p] + q * 16) = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+            for (int h = 0; h < RCH; ++h) {
+                // group of chunk h within the run
+                constexpr int CPG = G / CPC > 0 ? G / CPC : 1;   // chunks per group
+                const int gsel = NGT == 1 ? 0 : h / CPG;
+                float sf, zf;
+                if constexpr (MODE == AFFINE) {
+                    sf = bf16_bits_to_f32((sc[p] >> (16 * gsel)) & 0xFFFFu);
+                    zf = bf16_bits_to_f32((zc[p] >> (16 * gsel)) & 0xFFFFu);
+                } else {
+                    const uint32_t byte = (sc[p] >> (8 * gsel)) & 0xFFu;
+                    sf = MODE == NVFP4 ? e4m3_to_f32(byte) : e8m0_to_f32(byte);
+                    zf = 0.f;
+                }
+                Chunk<WORDS> ch;
+#pragma unroll
+                for (int q = 0; q < WORDS; ++q) ch.w[q] = wc[p].w[h * WORDS + q];
+                uint32_t o[CPC / 2];
+                dequant_chunk<MODE, BITS, WORDS>(ch, sf, zf, o);
+#pragma unroll
+                for (int q = 0; q < CPC / 8; ++q)
+                    *(u32x4*)(base + ldsoff[p] + h * CPC * 2 + q * 16) =
+                        u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+            }
         }
     };
 
@@ -315,35 +366,46 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         for (int s = 0; s < MT; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = a.K / BK;
-    // Register sets A and B hold packed codes for alternate steps.
-    Chunk<WORDS> wa[CPT], wb[CPT];
-    uint32_t sa[CPT], za[CPT], sb[CPT], zb[CPT];
+    // WPF register sets hold the packed codes of steps kt+1 .. kt+WPF; set
+    // u % WPF belongs to step u. The step loop is unrolled WPF times so set
+    // indices are compile-time.
+    Chunk<RWORDS> wset[WPF][CPT];
+    uint32_t sset[WPF][CPT], zset[WPF][CPT];
     unsigned char* const wbuf = smem + XST * XSTAGE;
 
-    // prologue: activations of steps 0 and 1 in flight, step 0's weights
-    // dequantized into buffer 0, step 1's codes in set A
+    // prologue: activations of steps 0 and 1 in flight, codes of steps
+    // 0 .. WPF-1 in flight, step 0's weights dequantized into buffer 0
     dma_x(0, 0);
-    load_w(wb, sb, zb, 0);
+    load_w(wset[0], sset[0], zset[0], 0);
     dma_x(1, nk > 1 ? 1 : 0);
-    load_w(wa, sa, za, nk > 1 ? 1 : 0);
-    store_w(wbuf, wb, sb, zb);   // waits for step 0's codes, hence for its activations
-    __syncthreads();
+    unroll<1, WPF>([&](auto u) {
+        constexpr int U = decltype(u)::value;
+        load_w(wset[U], sset[U], zset[U], U < nk ? U : nk - 1);
+    });
+    store_w(wbuf, wset[0], sset[0], zset[0]);  // waits for step 0's codes, hence its activations
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes done
+    asm volatile("s_barrier" ::: "memory");
 
-    // One step. Loads issued here land two steps later (activations) or are
-    // dequantized next step (codes). vm operations complete in order, so
-    // waiting until only this step's loads are outstanding means the
-    // activations for step kt+1 are in LDS. The step ends with that wait,
-    // lgkmcnt(0) (this wave's LDS writes done) and a plain s_barrier: a
-    // fenced barrier would also wait for this step's buffer->LDS loads.
-    constexpr int VM_PER_STEP = XDMA + CPT * (MODE == AFFINE ? 3 : 2);
-    static_assert(VM_PER_STEP < 64, "vmcnt range");
+    // One step. Activation loads issued here land two steps later, code
+    // loads WPF steps later. vm operations complete in order; at the end of
+    // step kt the activations of step kt+1 (issued at step kt-1) must be in
+    // LDS, so the wait leaves outstanding only what was issued after them:
+    // the code loads of step kt-1 and this step's loads. The step ends with
+    // that wait, lgkmcnt(0) (this wave's LDS writes done) and a plain
+    // s_barrier: a fenced barrier would also wait for this step's loads.
+    // code and scale loads per step (a 32-byte run takes two loads)
+    constexpr int WL = CPT * ((RWORDS == 8 ? 2 : 1) + (MODE == AFFINE ? 2 : 1));
+    constexpr int VM_ALLOWED = XDMA + WL + (WPF > 2 ? WL : 0);
+    static_assert(VM_ALLOWED < 64, "vmcnt range");
     // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-    constexpr int WAIT_IMM = (VM_PER_STEP & 15) | (7 << 4) | (0 << 8) | ((VM_PER_STEP >> 4) << 14);
-    auto step = [&](int kt, Chunk<WORDS> (&wc)[CPT], uint32_t (&sc)[CPT], uint32_t (&zc)[CPT],
-                    Chunk<WORDS> (&wn)[CPT], uint32_t (&sn)[CPT], uint32_t (&zn)[CPT]) {
-        const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;
-        dma_x((kt + 2) % XST, k2);
-        load_w(wn, sn, zn, k2);
+    constexpr int WAIT_IMM = (VM_ALLOWED & 15) | (7 << 4) | (0 << 8) | ((VM_ALLOWED >> 4) << 14);
+    auto step = [&](int kt, auto uc) {
+        constexpr int U = decltype(uc)::value;          // kt % WPF
+        constexpr int CUR = (U + 1) % WPF;              // set of step kt+1 (dequantized now)
+        const int kx = kt + 2 < nk ? kt + 2 : nk - 1;
+        const int kw = kt + WPF < nk ? kt + WPF : nk - 1;
+        dma_x((kt + 2) % XST, kx);
+        load_w(wset[U], sset[U], zset[U], kw);          // set U held step kt, dequantized last step
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* xt = smem + (kt % XST) * XSTAGE;
         const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
@@ -366,15 +428,15 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         // step kt+1's weights (beyond the last step this fills an unused
         // buffer), dequantized between the two halves of this step's MFMAs
         mma(0, 1);
-        store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wc, sc, zc);
+        store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wset[CUR], sset[CUR], zset[CUR]);
         mma(1, 2);
         __builtin_amdgcn_s_waitcnt(WAIT_IMM);
         asm volatile("s_barrier" ::: "memory");
     };
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, wa, sa, za, wb, sb, zb);
-        if (kt + 1 < nk) step(kt + 1, wb, sb, zb, wa, sa, za);
-    }
+    // the host picks WPF dividing the step count, so every unrolled step runs
+    // (a conditional step would blur the compiler's load-count bookkeeping)
+    for (int kt = 0; kt < nk; kt += WPF)
+        unroll<0, WPF>([&](auto u) { step(kt + decltype(u)::value, u); });
 
     // ---- epilogue: lane holds D[n = 4j + r][m = i] of each (t, s) tile
 #pragma unroll
@@ -400,21 +462,35 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     }
 }
 
+#ifndef QLIN_PREFILL_WPF
+#define QLIN_PREFILL_WPF 2
+#endif
+#ifndef QLIN_GATHER_WPF
+#define QLIN_GATHER_WPF 4
+#endif
+
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, bool GATHER>
 hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     // a chunk holds at least one packed dword
     constexpr int CPC = CPC0 < 32 / BITS ? 32 / BITS : CPC0;
+    constexpr int WPF = GATHER ? QLIN_GATHER_WPF : QLIN_PREFILL_WPF;
     const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
-    auto kern = qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER>;
-    static bool attr_set = false;  // per instantiation, host side
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    kern<<<grid, WM * WN * 64, shm, st>>>(t);
-    return hipGetLastError();
+    auto run = [&](auto kern) -> hipError_t {
+        static bool attr_set = false;  // per instantiation, host side
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(
+                (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        kern<<<grid, WM * WN * 64, shm, st>>>(t);
+        return hipGetLastError();
+    };
+    // the code prefetch depth must divide the number of 64-wide steps
+    const int nk = t.K / BK;
+    if (nk % WPF == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, WPF>);
+    if (nk % 2 == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 2>);
+    return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 1>);
 }
 
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0>
@@ -427,14 +503,14 @@ hipError_t launch_plain(const PrefillArgs& t, hipStream_t st) {
 // the most efficient per tile; 256 x 128 and 128 x 128 give more tiles when
 // the grid would not fill the chip. The choice minimises the tile area
 // times the number of rounds of 256 workgroups, with a per-shape efficiency.
-enum PrefillCfg { CFG_256x192 = 0, CFG_256x128 = 1, CFG_128x128 = 2 };
+enum PrefillCfg { CFG_256x192 = 0, CFG_256x128 = 1, CFG_128x128 = 2, CFG_128x256 = 3 };
 
 int pick_cfg(int64_t M, int64_t N) {
-    const int64_t bm[3] = {256, 256, 128}, bn[3] = {192, 128, 128};
-    const double eff[3] = {1.0, 0.95, 0.75};
+    const int64_t bm[4] = {256, 256, 128, 128}, bn[4] = {192, 128, 128, 256};
+    const double eff[4] = {1.0, 0.95, 0.75, 0.9};
     int best = 0;
     double best_cost = 0;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 4; ++c) {
         const int64_t tiles = ((M + bm[c] - 1) / bm[c]) * ((N + bn[c] - 1) / bn[c]);
         const double cost = (double)((tiles + 255) / 256) * (double)(bm[c] * bn[c]) / eff[c];
         if (c == 0 || cost < best_cost) {
@@ -457,10 +533,11 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     t.N = (int)q.N;
     t.K = (int)q.K;
     int cfg = pick_cfg(q.M, q.N);
-    if (const char* e = getenv("QLIN_PREFILL_TILE")) cfg = atoi(e) % 3;  // tests of each shape
+    if (const char* e = getenv("QLIN_PREFILL_TILE")) cfg = atoi(e) % 4;  // tests of each shape
     switch (cfg) {
     case CFG_256x128: return launch_plain<MODE, BITS, G, 256, 128, 4, 2, 8>(t, st);
     case CFG_128x128: return launch_plain<MODE, BITS, G, 128, 128, 2, 4, 8>(t, st);
+    case CFG_128x256: return launch_plain<MODE, BITS, G, 128, 256, 2, 4, 8>(t, st);
     default: return launch_plain<MODE, BITS, G, 256, 192, 4, 2, 8>(t, st);
     }
 }
@@ -485,11 +562,20 @@ hipError_t launch_gather_fmt(const QmmArgs& q, const uint32_t* perm, const uint3
     t.tiles = offsets + (q.E + 1);
     t.E = (int)q.E;
     t.B = (int)q.batch_x;
-    constexpr int BM = kPrefillGatherRows, BN = 192;
+#ifndef QLIN_GATHER_BN
+#define QLIN_GATHER_BN 192
+#endif
+    constexpr int BM = kPrefillGatherRows, BN = QLIN_GATHER_BN;
     // upper bound on row tiles: every expert may add one partial tile
     const int64_t mt = (q.R * q.M + BM - 1) / BM + q.E;
     const int grid = (int)(mt * ((q.N + BN - 1) / BN));
-    return launch_cfg<MODE, BITS, G, BM, BN, 2, 4, 8, true>(t, grid, st);
+#ifndef QLIN_GATHER_WAVES
+#define QLIN_GATHER_WAVES 0
+#endif
+    if constexpr (BM == 128 && QLIN_GATHER_WAVES == 1)
+        return launch_cfg<MODE, BITS, G, BM, BN, 4, 2, 8, true>(t, grid, st);
+    else
+        return launch_cfg<MODE, BITS, G, BM, BN, 2, 4, 8, true>(t, grid, st);
 }
 
 }  // namespace

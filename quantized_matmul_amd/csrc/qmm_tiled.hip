@@ -420,7 +420,7 @@ hipError_t launch_cfg(const TiledArgs& t, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-constexpr int GATHER_BM = 64;
+constexpr int GATHER_BM = kTiledGatherRows;
 
 template <int MODE, int BITS, int G>
 hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,
@@ -474,7 +474,7 @@ hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, i
     *perm = ws + 2 * (E + 1);
     const size_t shm = (size_t)2 * E * sizeof(uint32_t);
     if (shm > 64 * 1024) return hipErrorInvalidValue;
-    if (rows_per_tile != GATHER_BM) return hipErrorInvalidValue;  // tiles for this kernel's BM
+    if (rows_per_tile < 1) return hipErrorInvalidValue;
     bucket_kernel<<<1, 1024, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted, *offsets,
                                         *offsets + (E + 1), *perm);
     return hipGetLastError();

@@ -213,7 +213,7 @@ def test_prefill_kernel_affine(M, N, K, bits, g):
     run_qmm_case(M, N, K, bits, g, "affine", "bf16", True, path="prefill", wid=91 + bits)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
 @pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 128)])
 def test_prefill_kernel_tile_shapes(tile, bits, g):
     """Every tile shape of the many-row kernel, forced, on ragged M and N."""
