@@ -235,9 +235,15 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 // fragment order) and streams the remaining units through a PF-deep ring,
 // waiting only for the oldest unit. Waves meet once, for the final
 // cross-wave sum.
-template <int MODE, int BITS, int G, int UPW, int PF, int MREG>
+// DX (microscaled codes only, whose fragment order is the natural k order
+// in 16-byte or 8-byte pieces): instead of staging x in LDS, every lane loads
+// its A fragments from global memory together with the weight unit they
+// multiply; x of any size then fits one launch (the LDS keeps only the
+// cross-wave sums).
+template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX>
 __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
+    static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     constexpr int KW = UPW * F::U;                 // k per wave
     extern __shared__ __align__(16) unsigned char smem[];
     const int KS = (int)(blockDim.x >> 6);
@@ -245,7 +251,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     const int i = lane & 15, j = lane >> 4;
     const int K = a.K, M = a.M;
     const int rowb = xrow_bytes(K);
-    float* red = (float*)(smem + (M + 1) * rowb);  // [KS][16 rows][16 cols]
+    float* red = (float*)(smem + (DX ? 0 : (M + 1) * rowb));  // [KS][16 rows][16 cols]
 
     const int k0 = wv * KW;                       // first k of this wave
     const int u_begin = wv * UPW;
@@ -256,7 +262,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     const uint32_t* wrow = a.wq + (size_t)ncol * wpr + 4 * j;
     const size_t rowg = (size_t)ncol * gpr;
 
-    // ---- 1. this wave's x slice: M rows x KW elements, in blocks of BE
+    // ---- 1. this wave's x slice (staged path): M rows x KW elements, in blocks of BE
     // elements (the unit of the fragment-order permutation), spread over the
     // lanes; 16-byte chunks, at most XPL per lane
     constexpr int BE = F::XBLOCK;                  // elements per permutation block
@@ -265,14 +271,14 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     // takes (host guarantees M * KW <= 4096, i.e. at most 8)
     constexpr int MMAX = MREG == 4 ? 16 : MREG;
     constexpr int XNEED = (MMAX * KW + 511) / 512;
-    constexpr int XPL = ((XNEED < 8 ? XNEED : 8) + CPB - 1) / CPB * CPB;
+    constexpr int XPL = DX ? 0 : ((XNEED < 8 ? XNEED : 8) + CPB - 1) / CPB * CPB;
     const int xchunks = M * (KW / 8);              // host guarantees <= 64 * XPL
     // Buffer loads: chunks past the last row read as zero, so the loads need
     // no branch (a branch around a load makes the compiler drain every load
     // in flight, which would hold back the weight stream).
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.x), (short)0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
-    u32x4 xr[XPL];
+    u32x4 xr[XPL > 0 ? XPL : 1];
 #pragma unroll
     for (int c = 0; c < XPL; ++c) {
         // chunk id: lane-major within blocks so one lane owns whole blocks
@@ -318,7 +324,35 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    // ---- 3. the first PF weight units
+    // ---- this lane's A row (zero row when it carries no real x row)
+    int arow;
+    if constexpr (F::S == 2) arow = (i / 8 == j / 2 && (i & 7) < M) ? (i & 7) : M;
+    else arow = (i < M) ? i : M;
+
+    // DX: A fragments of unit u from global memory. Fragment of global step
+    // gs: k in [32 gs + 8 j, +8) for 4-bit codes; [32 gs + 4 j, +4) and
+    // [32 gs + 16 + 4 j, +4) for 8-bit codes. Rows >= M read zeros.
+    constexpr int XF = DX ? F::STEPS : 1;
+    const uint32_t xfoff = arow < M ? ((uint32_t)arow * (uint32_t)K + (BITS == 4 ? 8u : 4u) * j) * 2u
+                                    : 0x80000000u;
+    u32x4 xfr[DX ? PF : 1][XF];
+    auto load_xf = [&](u32x4 (&dst)[XF], int u) {
+        if constexpr (DX) {
+#pragma unroll
+            for (int ls = 0; ls < F::STEPS; ++ls) {
+                const int so = (u * F::STEPS + ls) * 64;  // bytes: 32 elements per step
+                if constexpr (BITS == 4) {
+                    dst[ls] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)xfoff, so, 0);
+                } else {
+                    const auto p0 = __builtin_amdgcn_raw_buffer_load_b64(xrs, (int)xfoff, so, 0);
+                    const auto p1 = __builtin_amdgcn_raw_buffer_load_b64(xrs, (int)xfoff, so + 32, 0);
+                    dst[ls] = u32x4{p0[0], p0[1], p1[0], p1[1]};
+                }
+            }
+        }
+    };
+
+    // ---- 3. the first PF weight units (and their x fragments)
     u32x4 wbuf[PF][F::RPU];
 #pragma unroll
     for (int p = 0; p < PF; ++p)
@@ -326,6 +360,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < F::RPU; ++r)
                 wbuf[p][r] = *(const u32x4*)(wrow + (size_t)((u_begin + p) * F::RPU + r) * 16);
+            if constexpr (DX) load_xf(xfr[p], u_begin + p);
         }
 
     // ---- 4. x slice -> LDS (fragment order) + this slice of the zero row
@@ -339,15 +374,12 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
             store_fragment_block<MODE, BITS>(dst, &xr[c]);
         }
     }
-    for (int q = lane; q < KW / 8; q += 64)
-        *(u32x4*)(smem + M * rowb + (k0 / 8 + q) * 16) = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (!DX)
+        for (int q = lane; q < KW / 8; q += 64)
+            *(u32x4*)(smem + M * rowb + (k0 / 8 + q) * 16) = u32x4{0u, 0u, 0u, 0u};
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (loads stay in flight)
     __builtin_amdgcn_wave_barrier();
 
-    // ---- this lane's A row (zero row when it carries no real x row)
-    int arow;
-    if constexpr (F::S == 2) arow = (i / 8 == j / 2 && (i & 7) < M) ? (i & 7) : M;
-    else arow = (i < M) ? i : M;
     const unsigned char* abase = smem + arow * rowb + j * 16;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dsum = {0.f, 0.f, 0.f, 0.f};
@@ -366,11 +398,17 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
             wcur[r] = wbuf[uu % PF][r];
             xpose4(wcur[r]);
         }
+        u32x4 xcur[XF];
+        if constexpr (DX) {
+#pragma unroll
+            for (int ls = 0; ls < XF; ++ls) xcur[ls] = xfr[uu % PF][ls];
+        }
         // refill the ring slot with unit uu + PF
         if (uu + PF < UPW) {
 #pragma unroll
             for (int r = 0; r < F::RPU; ++r)
                 wbuf[uu % PF][r] = *(const u32x4*)(wrow + (size_t)((u + PF) * F::RPU + r) * 16);
+            if constexpr (DX) load_xf(xfr[uu % PF], u + PF);
         }
 #pragma unroll
         for (int r = 0; r < F::RPU; ++r) {
@@ -378,7 +416,9 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
             for (int t = 0; t < F::SPR; ++t) {
                 const int ls = r * F::SPR + t;                 // step within unit
                 const int gs = (u * F::RPU + r) * F::SPR + t;  // global step
-                const u32x4 av = *(const u32x4*)(abase + gs * 64);
+                u32x4 av;
+                if constexpr (DX) av = xcur[ls];
+                else av = *(const u32x4*)(abase + gs * 64);
                 const bool first = F::AFF && (ls % F::WS == 0);
                 if constexpr (F::AFF) dsum = mfma_bf16(av, ones, first ? zero4 : dsum);
                 float sc = 0.f;
@@ -448,20 +488,22 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
 #endif
 
 template <int MODE, int BITS, int G>
-int pick_upw(int nunits, int M) {
+int pick_upw(int nunits, int M, bool dx) {
     using F = Fmt<MODE, BITS, G>;
+    // the staged path keeps a wave's x slice in at most 8 chunk registers
+    const int xlim = dx ? (1 << 30) : 4096;
     int upw = F::RPU >= 2 ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
-    while (upw > 1 && (nunits % upw || M * upw * F::U > 4096)) upw >>= 1;
-    if (nunits % upw || M * upw * F::U > 4096 || nunits / upw > 16) return 0;
+    while (upw > 1 && (nunits % upw || M * upw * F::U > xlim)) upw >>= 1;
+    if (nunits % upw || M * upw * F::U > xlim || nunits / upw > 16) return 0;
     return upw;
 }
 
-template <int MODE, int BITS, int G, int UPW>
+template <int MODE, int BITS, int G, int UPW, bool DX>
 hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
     constexpr int PF = UPW < QLIN_DECODE_PF ? UPW : QLIN_DECODE_PF;
     const unsigned blocks = (unsigned)((a.N + 15) / 16);
     const unsigned threads = 64u * (unsigned)ks;
-    const size_t shm = (size_t)(a.M + 1) * xrow_bytes(a.K) + (size_t)ks * 16 * 16 * 4;
+    const size_t shm = (DX ? 0 : (size_t)(a.M + 1) * xrow_bytes(a.K)) + (size_t)ks * 16 * 16 * 4;
     auto run = [&](auto kern) -> hipError_t {
         if (shm > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -471,12 +513,12 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
         kern<<<blocks, threads, shm, st>>>(a);
         return hipGetLastError();
     };
-    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1>);
-    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2>);
-    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4>);
+    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX>);
+    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX>);
+    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX>);
 }
 
-template <int MODE, int BITS, int G>
+template <int MODE, int BITS, int G, bool DX>
 hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     using F = Fmt<MODE, BITS, G>;
     DecodeArgs a;
@@ -490,17 +532,17 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     a.K = (int)q.K;
     const int mreg = a.M > 4 ? 4 : a.M;
     const int nunits = a.K / F::U;
-    const int upw = pick_upw<MODE, BITS, G>(nunits, a.M);
+    const int upw = pick_upw<MODE, BITS, G>(nunits, a.M, DX);
     if (upw == 0) return hipErrorNotSupported;
     const int ks = nunits / upw;
     switch (upw) {
 #if QLIN_DECODE_UPW_MAX >= 16
-    case 16: return launch_upw<MODE, BITS, G, (F::RPU >= 2 ? 8 : 16)>(a, ks, mreg, st);
+    case 16: return launch_upw<MODE, BITS, G, (F::RPU >= 2 ? 8 : 16), DX>(a, ks, mreg, st);
 #endif
-    case 8: return launch_upw<MODE, BITS, G, 8>(a, ks, mreg, st);
-    case 4: return launch_upw<MODE, BITS, G, 4>(a, ks, mreg, st);
-    case 2: return launch_upw<MODE, BITS, G, 2>(a, ks, mreg, st);
-    default: return launch_upw<MODE, BITS, G, 1>(a, ks, mreg, st);
+    case 8: return launch_upw<MODE, BITS, G, 8, DX>(a, ks, mreg, st);
+    case 4: return launch_upw<MODE, BITS, G, 4, DX>(a, ks, mreg, st);
+    case 2: return launch_upw<MODE, BITS, G, 2, DX>(a, ks, mreg, st);
+    default: return launch_upw<MODE, BITS, G, 1, DX>(a, ks, mreg, st);
     }
 }
 
@@ -510,26 +552,63 @@ namespace {
 
 constexpr size_t kDecodeLdsLimit = 150 * 1024;
 
-// Shape rules of the decode kernel for m activation rows (see pick_upw()).
-bool decode_shape_ok(const QmmArgs& q, int64_t m) {
+int decode_upw(const QmmArgs& q, int64_t m, bool dx) {
     const int per = 32 / q.bits;
     const int rk = 16 * per;
     const int u = rk > q.group_size ? rk : q.group_size;
-    if (q.K % u != 0) return false;
-    if (q.mode == AFFINE && q.bits == 2 && q.group_size == 32 && m > 8) return false;
+    if (q.K % u != 0) return 0;
     const int nunits = (int)(q.K / u);
+    const int64_t xlim = dx ? (1LL << 30) : 4096;
     int upw = (u / rk >= 2) ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
-    while (upw > 1 && (nunits % upw || m * upw * u > 4096)) upw >>= 1;
-    if (nunits % upw || m * upw * u > 4096 || nunits / upw > 16) return false;
+    while (upw > 1 && (nunits % upw || m * upw * u > xlim)) upw >>= 1;
+    if (nunits % upw || m * upw * u > xlim || nunits / upw > 16) return 0;
+    return upw;
+}
+
+// Shape rules of the staged decode kernel for m activation rows.
+bool decode_shape_ok(const QmmArgs& q, int64_t m) {
+    if (q.mode == AFFINE && q.bits == 2 && q.group_size == 32 && m > 8) return false;
+    if (decode_upw(q, m, false) == 0) return false;
     const size_t shm = (size_t)(m + 1) * xrow_bytes((int)q.K) + 16 * 16 * 16 * 4;
     return shm <= kDecodeLdsLimit;
 }
 
-// Largest number of activation rows one launch takes (0: none).
+// Largest number of activation rows one staged launch takes (0: none).
 int64_t decode_rows_per_pass(const QmmArgs& q) {
     for (int64_t m = q.M < 16 ? q.M : 16; m >= 1; --m)
         if (decode_shape_ok(q, m)) return m;
     return 0;
+}
+
+// Microscaled codes unpack in natural k order, so when x does not fit one
+// staged launch the A fragments come straight from global memory instead.
+bool decode_direct_x(const QmmArgs& q) {
+    return q.mode != AFFINE && decode_rows_per_pass(q) < q.M && decode_upw(q, q.M, true) > 0;
+}
+
+template <bool DX>
+hipError_t launch_mode(const QmmArgs& q, hipStream_t st) {
+    switch (q.mode) {
+    case MXFP4: return launch_fmt<MXFP4, 4, 32, DX>(q, st);
+    case NVFP4: return launch_fmt<NVFP4, 4, 16, DX>(q, st);
+    case MXFP8: return launch_fmt<MXFP8, 8, 32, DX>(q, st);
+    default: break;
+    }
+    if constexpr (DX) {
+        return hipErrorNotSupported;
+    } else {
+        if (q.bits == 4)
+            return q.group_size == 32 ? launch_fmt<AFFINE, 4, 32, false>(q, st)
+                 : q.group_size == 64 ? launch_fmt<AFFINE, 4, 64, false>(q, st)
+                                      : launch_fmt<AFFINE, 4, 128, false>(q, st);
+        if (q.bits == 8)
+            return q.group_size == 32 ? launch_fmt<AFFINE, 8, 32, false>(q, st)
+                 : q.group_size == 64 ? launch_fmt<AFFINE, 8, 64, false>(q, st)
+                                      : launch_fmt<AFFINE, 8, 128, false>(q, st);
+        return q.group_size == 32 ? launch_fmt<AFFINE, 2, 32, false>(q, st)
+             : q.group_size == 64 ? launch_fmt<AFFINE, 2, 64, false>(q, st)
+                                  : launch_fmt<AFFINE, 2, 128, false>(q, st);
+    }
 }
 
 }  // namespace
@@ -537,11 +616,13 @@ int64_t decode_rows_per_pass(const QmmArgs& q) {
 bool qmm_decode_supports(const QmmArgs& q) {
     if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R != 0) return false;
     if (q.M < 1 || q.M > 16 || q.N < 1 || q.K > (1 << 20)) return false;
+    if (q.M * q.K * 2 >= (1LL << 31)) return false;  // 32-bit buffer offsets into x
     // 16-byte aligned weight rows, x rows and per-wave scale blocks
     if (((uintptr_t)q.wq & 15) != 0 || ((uintptr_t)q.x & 15) != 0) return false;
     if (((uintptr_t)q.scales & 15) != 0 || ((uintptr_t)q.biases & 15) != 0) return false;
     const int64_t gpr = q.K / q.group_size;
     if ((q.mode == AFFINE ? gpr * 2 : gpr) % 16 != 0) return false;
+    if (decode_direct_x(q)) return true;
     // x rows that do not fit one launch's LDS run as several launches, each
     // streaming the weight again (at most 4)
     const int64_t rpp = decode_rows_per_pass(q);
@@ -550,32 +631,14 @@ bool qmm_decode_supports(const QmmArgs& q) {
 
 hipError_t launch_qmm_decode(const QmmArgs& q0, hipStream_t st) {
     if (!qmm_decode_supports(q0)) return hipErrorNotSupported;
+    if (decode_direct_x(q0)) return launch_mode<true>(q0, st);
     const int64_t rpp = decode_rows_per_pass(q0);
     for (int64_t m0 = 0; m0 < q0.M; m0 += rpp) {
         QmmArgs q = q0;
         q.M = (q0.M - m0) < rpp ? (q0.M - m0) : rpp;
         q.x = (const uint16_t*)q0.x + m0 * q0.K;
         q.y = (uint16_t*)q0.y + m0 * q0.N;
-        hipError_t e;
-        switch (q.mode) {
-        case MXFP4: e = launch_fmt<MXFP4, 4, 32>(q, st); break;
-        case NVFP4: e = launch_fmt<NVFP4, 4, 16>(q, st); break;
-        case MXFP8: e = launch_fmt<MXFP8, 8, 32>(q, st); break;
-        default:
-            if (q.bits == 4) {
-                e = q.group_size == 32 ? launch_fmt<AFFINE, 4, 32>(q, st)
-                  : q.group_size == 64 ? launch_fmt<AFFINE, 4, 64>(q, st)
-                                       : launch_fmt<AFFINE, 4, 128>(q, st);
-            } else if (q.bits == 8) {
-                e = q.group_size == 32 ? launch_fmt<AFFINE, 8, 32>(q, st)
-                  : q.group_size == 64 ? launch_fmt<AFFINE, 8, 64>(q, st)
-                                       : launch_fmt<AFFINE, 8, 128>(q, st);
-            } else {
-                e = q.group_size == 32 ? launch_fmt<AFFINE, 2, 32>(q, st)
-                  : q.group_size == 64 ? launch_fmt<AFFINE, 2, 64>(q, st)
-                                       : launch_fmt<AFFINE, 2, 128>(q, st);
-            }
-        }
+        hipError_t e = launch_mode<false>(q, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

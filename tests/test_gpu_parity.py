@@ -184,8 +184,10 @@ def test_decode_kernel_micro(M, mode, g, bits):
 
 @pytest.mark.parametrize("M", [9, 16])
 def test_decode_kernel_row_passes(M):
-    """x rows too large for one launch's LDS run as several passes."""
-    run_qmm_case(M, 64, 8192, 4, 32, "mxfp4", "bf16", True, path="decode", wid=32)
+    """x rows too large for one launch's LDS: affine runs several passes,
+    microscaled codes take their x fragments straight from global memory."""
+    for mode, g, bits in MICRO_CASES:
+        run_qmm_case(M, 64, 8192, bits, g, mode, "bf16", True, path="decode", wid=32)
     run_qmm_case(M, 40, 8192, 4, 64, "affine", "bf16", True, path="decode", wid=33)
 
 
