@@ -41,6 +41,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -172,6 +173,7 @@ struct DecodeArgs {
     const uint16_t* biases;
     uint16_t* y;         // bf16 [M, N]
     int M, N, K;
+    int cols;            // output columns per workgroup (<= 16, the MFMA width)
 };
 
 // LDS layout: (M+1) rows of K/8 16-byte chunks (row M is zero), each row
@@ -255,12 +257,20 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
 
     const int k0 = wv * KW;                       // first k of this wave
     const int u_begin = wv * UPW;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * a.cols;
     const int wpr = K / F::PER;                   // words per weight row
     const int gpr = K / G;                        // groups per weight row
-    const int ncol = min(n0 + i, a.N - 1);        // ragged N: re-read the last row, never stored
-    const uint32_t* wrow = a.wq + (size_t)ncol * wpr + 4 * j;
-    const size_t rowg = (size_t)ncol * gpr;
+    // Lane row i carries output column n0 + i. Columns past this workgroup's
+    // share (or past N) read zeros through the buffer range check: no memory
+    // traffic, never stored.
+    const bool colv = i < a.cols && n0 + i < a.N;
+    const uint32_t ncol = (uint32_t)(n0 + i);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(a.wq), (short)0, (int)((uint32_t)a.N * (uint32_t)wpr * 4u), 0x00020000);
+    const uint32_t woff = colv ? (ncol * (uint32_t)wpr + 4u * j) * 4u : 0x80000000u;
+    auto wload = [&](int unit_region) -> u32x4 {   // 16 bytes of region (u * RPU + r)
+        return __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)woff, unit_region * 64, 0);
+    };
 
     // ---- 1. this wave's x slice (staged path): M rows x KW elements, in blocks of BE
     // elements (the unit of the fragment-order permutation), spread over the
@@ -296,30 +306,38 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     constexpr int SW = (SB + 3) / 4;
     uint32_t sraw[SW], zraw[F::AFF ? SW : 1];
     {
-        const size_t gfirst = rowg + (size_t)u_begin * F::GPU;
-        const unsigned char* sp = F::AFF ? (const unsigned char*)a.scales + gfirst * 2
-                                         : (const unsigned char*)a.scales + gfirst;
-        const unsigned char* zp = (const unsigned char*)a.biases + gfirst * 2;
+        constexpr uint32_t SBYTES = F::AFF ? 2u : 1u;
+        const uint32_t sbytes_all = (uint32_t)a.N * (uint32_t)gpr * SBYTES;
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(a.scales), (short)0, (int)sbytes_all, 0x00020000);
+        const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(F::AFF ? a.biases : (const uint16_t*)a.scales), (short)0,
+            (int)(F::AFF ? sbytes_all : 0u), 0x00020000);
+        const uint32_t soff = colv ? (ncol * (uint32_t)gpr + (uint32_t)(u_begin * F::GPU)) * SBYTES
+                                   : 0x80000000u;
         if constexpr (SB >= 16) {
 #pragma unroll
             for (int v = 0; v < SB / 16; ++v) {
-                const u32x4 t = *(const u32x4*)(sp + 16 * v);
+                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)soff, 16 * v, 0);
                 sraw[4 * v] = t[0]; sraw[4 * v + 1] = t[1]; sraw[4 * v + 2] = t[2]; sraw[4 * v + 3] = t[3];
                 if constexpr (F::AFF) {
-                    const u32x4 tz = *(const u32x4*)(zp + 16 * v);
+                    const u32x4 tz = __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)soff, 16 * v, 0);
                     zraw[4 * v] = tz[0]; zraw[4 * v + 1] = tz[1]; zraw[4 * v + 2] = tz[2]; zraw[4 * v + 3] = tz[3];
                 }
             }
         } else if constexpr (SB == 8) {
-            const uint2 t = *(const uint2*)sp;
-            sraw[0] = t.x; sraw[1] = t.y;
-            if constexpr (F::AFF) { const uint2 tz = *(const uint2*)zp; zraw[0] = tz.x; zraw[1] = tz.y; }
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(srs, (int)soff, 0, 0);
+            sraw[0] = t[0]; sraw[1] = t[1];
+            if constexpr (F::AFF) {
+                const u32x2 tz = __builtin_amdgcn_raw_buffer_load_b64(zrs, (int)soff, 0, 0);
+                zraw[0] = tz[0]; zraw[1] = tz[1];
+            }
         } else if constexpr (SB == 4) {
-            sraw[0] = *(const uint32_t*)sp;
-            if constexpr (F::AFF) zraw[0] = *(const uint32_t*)zp;
+            sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)soff, 0, 0);
+            if constexpr (F::AFF) zraw[0] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)soff, 0, 0);
         } else {
-            sraw[0] = *(const uint16_t*)sp;
-            if constexpr (F::AFF) zraw[0] = *(const uint16_t*)zp;
+            sraw[0] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)soff, 0, 0);
+            if constexpr (F::AFF) zraw[0] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)soff, 0, 0);
         }
     }
 
@@ -359,7 +377,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
         if (p < UPW) {
 #pragma unroll
             for (int r = 0; r < F::RPU; ++r)
-                wbuf[p][r] = *(const u32x4*)(wrow + (size_t)((u_begin + p) * F::RPU + r) * 16);
+                wbuf[p][r] = wload((u_begin + p) * F::RPU + r);
             if constexpr (DX) load_xf(xfr[p], u_begin + p);
         }
 
@@ -407,7 +425,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
         if (uu + PF < UPW) {
 #pragma unroll
             for (int r = 0; r < F::RPU; ++r)
-                wbuf[uu % PF][r] = *(const u32x4*)(wrow + (size_t)((u + PF) * F::RPU + r) * 16);
+                wbuf[uu % PF][r] = wload((u + PF) * F::RPU + r);
             if constexpr (DX) load_xf(xfr[uu % PF], u + PF);
         }
 #pragma unroll
@@ -462,7 +480,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     for (int o = tid; o < M * 16; o += 64 * KS) {
         const int m = o >> 4, col = o & 15;
         const int n = n0 + col;
-        if (n >= a.N) continue;
+        if (n >= a.N || col >= a.cols) continue;
         float v = 0.f;
         for (int w = 0; w < KS; ++w) {
             if constexpr (F::S == 2) {
@@ -487,6 +505,28 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
 #define QLIN_DECODE_PF 4        // weight units in flight per wave
 #endif
 
+// Output columns per workgroup: all workgroups of a launch are resident at
+// once, so a CU's share is ceil(workgroups / 256) of them; take the widest
+// block (at most the 16 MFMA columns) that minimises the columns per CU.
+// N = 14336: 14 columns, 1024 workgroups, 4 per CU (16 columns would give
+// half the CUs 4 workgroups and half 3).
+#ifndef QLIN_DECODE_CUS
+#define QLIN_DECODE_CUS 256
+#endif
+int decode_columns(int N) {
+    int best = 16;
+    int64_t best_load = 0;
+    for (int c = 16; c >= 8; --c) {
+        const int64_t wgs = (N + c - 1) / c;
+        const int64_t load = (wgs + QLIN_DECODE_CUS - 1) / QLIN_DECODE_CUS * c;
+        if (c == 16 || load < best_load) {
+            best = c;
+            best_load = load;
+        }
+    }
+    return best;
+}
+
 template <int MODE, int BITS, int G>
 int pick_upw(int nunits, int M, bool dx) {
     using F = Fmt<MODE, BITS, G>;
@@ -501,7 +541,7 @@ int pick_upw(int nunits, int M, bool dx) {
 template <int MODE, int BITS, int G, int UPW, bool DX>
 hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
     constexpr int PF = UPW < QLIN_DECODE_PF ? UPW : QLIN_DECODE_PF;
-    const unsigned blocks = (unsigned)((a.N + 15) / 16);
+    const unsigned blocks = (unsigned)((a.N + a.cols - 1) / a.cols);
     const unsigned threads = 64u * (unsigned)ks;
     const size_t shm = (DX ? 0 : (size_t)(a.M + 1) * xrow_bytes(a.K)) + (size_t)ks * 16 * 16 * 4;
     auto run = [&](auto kern) -> hipError_t {
@@ -530,6 +570,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
+    a.cols = decode_columns(a.N);
     const int mreg = a.M > 4 ? 4 : a.M;
     const int nunits = a.K / F::U;
     const int upw = pick_upw<MODE, BITS, G>(nunits, a.M, DX);
@@ -616,7 +657,9 @@ hipError_t launch_mode(const QmmArgs& q, hipStream_t st) {
 bool qmm_decode_supports(const QmmArgs& q) {
     if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R != 0) return false;
     if (q.M < 1 || q.M > 16 || q.N < 1 || q.K > (1 << 20)) return false;
-    if (q.M * q.K * 2 >= (1LL << 31)) return false;  // 32-bit buffer offsets into x
+    // 32-bit buffer offsets into x, the weight and its scales
+    if (q.M * q.K * 2 >= (1LL << 31) || q.N * q.K * q.bits / 8 >= (1LL << 31)) return false;
+    if (q.N * (q.K / q.group_size) * 2 >= (1LL << 31)) return false;
     // 16-byte aligned weight rows, x rows and per-wave scale blocks
     if (((uintptr_t)q.wq & 15) != 0 || ((uintptr_t)q.x & 15) != 0) return false;
     if (((uintptr_t)q.scales & 15) != 0 || ((uintptr_t)q.biases & 15) != 0) return false;
