@@ -52,10 +52,17 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     const int rr = lane / WPB, cl = lane % WPB;
     const int K = a.K, N = a.N;
     const int wcols = N / PER;                        // packed words per W row
-    const int c = blockIdx.x * WPB + cl;              // word column of the lane
+    // Workgroups are dealt to the 8 XCDs round-robin. Neighbouring column
+    // blocks share 128-byte lines of every weight row (a block uses WPB words
+    // of a row), so renumber the blocks: each XCD walks a contiguous run of
+    // them and the shared lines meet in that XCD's L2 instead of being
+    // fetched once per XCD.
+    int cb = blockIdx.x;
+    if ((gridDim.x & 7) == 0) cb = (cb & 7) * (gridDim.x >> 3) + (cb >> 3);
+    const int c = cb * WPB + cl;                      // word column of the lane
     const bool active = c < wcols;
     const int gpr = N / G;                            // groups per W row
-    const int g0 = (blockIdx.x * WPB * PER) / G;      // first group of the workgroup
+    const int g0 = (cb * WPB * PER) / G;              // first group of the workgroup
     const int gl = active ? (c * PER) / G - g0 : 0;   // the lane's group, local
 
     // LDS: x [MR][K] bf16 | scales [K][GW] | biases [K][GW]
@@ -227,7 +234,7 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
         __syncthreads();
         for (int o = tid; o < WPB * PER; o += 64 * NWAVES) {
             const int l = o / PER, e = o - l * PER;
-            const int cc = blockIdx.x * WPB + l;
+            const int cc = cb * WPB + l;
             float v = 0.f;
 #pragma unroll 4
             for (int w = 0; w < NWAVES; ++w) v += red[(w * WPB + l) * PER + e];
@@ -247,10 +254,14 @@ inline int nt_mr(int M) { return M <= 2 ? M : (M <= 4 ? 4 : 8); }
 #define QLIN_NT_NW 16
 #endif
 
+// waves per workgroup: 16 for up to 4 activation rows, 8 for more (the
+// register ring then holds more accumulators per lane)
+inline int nt_waves(int M) { return nt_mr(M) == 8 ? 8 : QLIN_NT_NW; }
+
 inline size_t nt_shm(int M, int K, int per, int G, bool aff) {
     const int wpb = QLIN_NT_WPB;
     const int gw = (wpb * per) >= G ? (wpb * per) / G : 1;
-    const size_t red_bytes = (size_t)QLIN_NT_NW * wpb * per * 4;
+    const size_t red_bytes = (size_t)nt_waves(M) * wpb * per * 4;
     const size_t stage = (size_t)nt_mr(M) * K * 2 + (size_t)K * gw * (aff ? 4 : 1);
     return stage > red_bytes ? stage : red_bytes;
 }
@@ -271,20 +282,20 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     constexpr int WPB = QLIN_NT_WPB, NW = QLIN_NT_NW;
     const unsigned blocks = (unsigned)((wcols + WPB - 1) / WPB);
     const size_t shm = nt_shm(a.M, a.K, PER, G, MODE == AFFINE);
-    auto run = [&](auto kern) -> hipError_t {
+    auto run = [&](auto kern, int nw) -> hipError_t {
         if (shm > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
             if (e != hipSuccess) return e;
         }
-        kern<<<blocks, 64 * NW, shm, st>>>(a);
+        kern<<<blocks, 64 * nw, shm, st>>>(a);
         return hipGetLastError();
     };
     switch (nt_mr(a.M)) {
-    case 1: return run(qmm_nt_kernel<MODE, BITS, G, 1, WPB, NW>);
-    case 2: return run(qmm_nt_kernel<MODE, BITS, G, 2, WPB, NW>);
-    case 4: return run(qmm_nt_kernel<MODE, BITS, G, 4, WPB, NW>);
-    default: return run(qmm_nt_kernel<MODE, BITS, G, 8, WPB, NW>);
+    case 1: return run(qmm_nt_kernel<MODE, BITS, G, 1, WPB, NW>, NW);
+    case 2: return run(qmm_nt_kernel<MODE, BITS, G, 2, WPB, NW>, NW);
+    case 4: return run(qmm_nt_kernel<MODE, BITS, G, 4, WPB, NW>, NW);
+    default: return run(qmm_nt_kernel<MODE, BITS, G, 8, WPB, 8>, 8);
     }
 }
 
