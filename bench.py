@@ -10,9 +10,11 @@ measured in the same run and reported alongside.
 Timing: inputs resident in HBM; decode steps cycle through >= 512 MB of
 distinct weight copies so that the 256 MB Infinity Cache cannot serve them;
 the timed launches are captured in a HIP graph (no host overhead between
-kernels) and bracketed by torch.cuda.synchronize() and HIP events on the
-launch stream. Algorithmic bytes = packed W + scales + biases + x + y, each
-counted once; flops = 2*M*N*K.
+kernels), replayed once untimed, then replayed LOOPS = 5 times, each replay
+of exactly `steps` launches bracketed by torch.cuda.synchronize() and HIP
+events on the launch stream; the median replay is reported. Algorithmic
+bytes = packed W + scales + biases + x + y, each counted once; flops =
+2*M*N*K.
 
 cpu_baseline: the CPU oracle (test infrastructure, plain C, fp64) on a
 bounded sample of the same decode workload, timed on this host.
@@ -32,6 +34,7 @@ METRIC = "qmm decode GB/s (% of HBM peak) + prefill TFLOP/s; int4 g64 affine"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
 ROTATE_BYTES = 512 * 2 ** 20
+LOOPS = 5  # timed loops per workload; the median is reported
 
 
 def parse():
@@ -95,12 +98,19 @@ def main():
                     fn_list[s % len(fn_list)]()
             g.replay()  # warm replay
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
+            # LOOPS timed replays of exactly `steps` launches each; the median
+            # loop is reported (the first loop after a pause runs on cooler
+            # clocks)
+            times = []
+            for _ in range(LOOPS):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = sorted(times)[len(times) // 2]
             del g
         else:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

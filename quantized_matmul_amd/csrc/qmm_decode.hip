@@ -494,12 +494,11 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     }
 }
 
-// Decomposition: a wave's slice is KW = UPW units; the host picks the
-// largest power-of-two UPW (<= 8, or 4 for two-region units) dividing the
-// unit count such that the wave's x slice fits 8 chunk registers per lane
-// (M * KW <= 4096) and KS = nunits / UPW <= 16 waves.
+// Decomposition: a wave's slice is KW = UPW units (choose_upw below); a
+// workgroup has KS = nunits / UPW <= 16 waves. Shorter slices (more waves per
+// workgroup) measured faster: UPW 4 beats 8 by about 5 % at M = 1.
 #ifndef QLIN_DECODE_UPW_MAX
-#define QLIN_DECODE_UPW_MAX 8   // units per wave (power of two, <= 16)
+#define QLIN_DECODE_UPW_MAX 4   // units per wave (power of two, <= 16)
 #endif
 #ifndef QLIN_DECODE_PF
 #define QLIN_DECODE_PF 4        // weight units in flight per wave
@@ -527,15 +526,24 @@ int decode_columns(int N) {
     return best;
 }
 
+// Units per wave: start from QLIN_DECODE_UPW_MAX (half that for two-region
+// units), grow while the workgroup would need more than 16 waves, then
+// shrink until it divides the unit count and (staged path) the wave's x
+// slice fits 8 chunk registers per lane. 0: no valid decomposition.
+int choose_upw(int nunits, int64_t M, int U, int RPU, bool dx) {
+    const int64_t xlim = dx ? (1LL << 40) : 4096;
+    int upw = RPU >= 2 ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
+    if (upw < 1) upw = 1;
+    while (upw < 16 && nunits / upw > 16) upw <<= 1;
+    while (upw > 1 && (nunits % upw || M * upw * U > xlim)) upw >>= 1;
+    if (nunits % upw || M * upw * U > xlim || nunits / upw > 16) return 0;
+    return upw;
+}
+
 template <int MODE, int BITS, int G>
 int pick_upw(int nunits, int M, bool dx) {
     using F = Fmt<MODE, BITS, G>;
-    // the staged path keeps a wave's x slice in at most 8 chunk registers
-    const int xlim = dx ? (1 << 30) : 4096;
-    int upw = F::RPU >= 2 ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
-    while (upw > 1 && (nunits % upw || M * upw * F::U > xlim)) upw >>= 1;
-    if (nunits % upw || M * upw * F::U > xlim || nunits / upw > 16) return 0;
-    return upw;
+    return choose_upw(nunits, M, F::U, F::RPU, dx);
 }
 
 template <int MODE, int BITS, int G, int UPW, bool DX>
@@ -577,9 +585,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     if (upw == 0) return hipErrorNotSupported;
     const int ks = nunits / upw;
     switch (upw) {
-#if QLIN_DECODE_UPW_MAX >= 16
-    case 16: return launch_upw<MODE, BITS, G, (F::RPU >= 2 ? 8 : 16), DX>(a, ks, mreg, st);
-#endif
+    case 16: return launch_upw<MODE, BITS, G, 16, DX>(a, ks, mreg, st);
     case 8: return launch_upw<MODE, BITS, G, 8, DX>(a, ks, mreg, st);
     case 4: return launch_upw<MODE, BITS, G, 4, DX>(a, ks, mreg, st);
     case 2: return launch_upw<MODE, BITS, G, 2, DX>(a, ks, mreg, st);
@@ -598,12 +604,7 @@ int decode_upw(const QmmArgs& q, int64_t m, bool dx) {
     const int rk = 16 * per;
     const int u = rk > q.group_size ? rk : q.group_size;
     if (q.K % u != 0) return 0;
-    const int nunits = (int)(q.K / u);
-    const int64_t xlim = dx ? (1LL << 30) : 4096;
-    int upw = (u / rk >= 2) ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
-    while (upw > 1 && (nunits % upw || m * upw * u > xlim)) upw >>= 1;
-    if (nunits % upw || m * upw * u > xlim || nunits / upw > 16) return 0;
-    return upw;
+    return choose_upw((int)(q.K / u), m, u, u / rk, dx);
 }
 
 // Shape rules of the staged decode kernel for m activation rows.
