@@ -161,6 +161,13 @@ __device__ __forceinline__ u32x4 unpack(const u32x4& w, int t, float sc) {
     return b;
 }
 
+// Value of another lane of the same DPP row (ctrl: a quad_perm or mirror pattern).
+template <int CTRL>
+__device__ __forceinline__ float lane_xchg(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
 template <int MODE>
 __device__ __forceinline__ float scale_byte_to_f32(uint32_t byte) {
     return MODE == NVFP4 ? e4m3_to_f32(byte) : e8m0_to_f32(byte);
@@ -242,14 +249,18 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 // its A fragments from global memory together with the weight unit they
 // multiply; x of any size then fits one launch (the LDS keeps only the
 // cross-wave sums).
-template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX>
+template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS>
 __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
+    static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
     constexpr int KW = UPW * F::U;                 // k per wave
     extern __shared__ __align__(16) unsigned char smem[];
     const int KS = (int)(blockDim.x >> 6);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: the weight loads take per-wave offsets in the
+    // scalar offset operand, which must be provably wave-uniform
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, j = lane >> 4;
     const int K = a.K, M = a.M;
     const int rowb = xrow_bytes(K);
@@ -279,7 +290,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     constexpr int CPB = BE / 8;                    // chunks per block
     // chunk registers per lane: enough for the most rows this instantiation
     // takes (host guarantees M * KW <= 4096, i.e. at most 8)
-    constexpr int MMAX = MREG == 4 ? 16 : MREG;
+    constexpr int MMAX = (MREG == 4 && !XS) ? 16 : MREG;
     constexpr int XNEED = (MMAX * KW + 511) / 512;
     constexpr int XPL = DX ? 0 : ((XNEED < 8 ? XNEED : 8) + CPB - 1) / CPB * CPB;
     const int xchunks = M * (KW / 8);              // host guarantees <= 64 * XPL
@@ -395,6 +406,42 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     if constexpr (!DX)
         for (int q = lane; q < KW / 8; q += 64)
             *(u32x4*)(smem + M * rowb + (k0 / 8 + q) * 16) = u32x4{0u, 0u, 0u, 0u};
+
+    // XS (at most 4 rows): sum x over every quantization group of the slice
+    // once, from the chunks this lane loaded (a permutation block of BE
+    // elements per lane, G / BE consecutive lanes per group), instead of a
+    // second MFMA against an all-ones operand per K-step. Every lane of a
+    // group ends with the group's sum; the epilogue reads it with readlane
+    // (rows < 4 are the only rows a lane row j = 0 holds, and rows of other
+    // lane rows are past M and never stored).
+    constexpr int NB = XS ? XPL / CPB : 1;
+    float bsum[NB];
+    if constexpr (XS) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t = 0.f;
+#pragma unroll
+            for (int part = 0; part < CPB; ++part) {
+                const u32x4 c = xr[b * CPB + part];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    t += bf16_bits_to_f32(c[e] & 0xFFFFu) + bf16_bits_to_f32(c[e] >> 16);
+            }
+            constexpr int LG = G / BE;  // lanes per group
+            if constexpr (LG >= 2) t += lane_xchg<0xB1>(t);   // quad_perm [1,0,3,2]
+            if constexpr (LG >= 4) t += lane_xchg<0x4E>(t);   // quad_perm [2,3,0,1]
+            if constexpr (LG >= 8) t += lane_xchg<0x141>(t);  // row_half_mirror
+            if constexpr (LG >= 16) t += lane_xchg<0x140>(t); // row_mirror
+            bsum[b] = t;
+        }
+    }
+    // sum of x row m over local group gl of this wave's slice (XS only)
+    auto xgroup_sum = [&](int m, int gl) -> float {
+        const int cid0 = m * (KW / 8) + gl * (G / 8);
+        const int blk0 = cid0 / CPB;
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, bsum[(blk0 / 64) < NB ? blk0 / 64 : 0]), blk0 % 64));
+    };
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (loads stay in flight)
     __builtin_amdgcn_wave_barrier();
 
@@ -438,7 +485,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
                 if constexpr (DX) av = xcur[ls];
                 else av = *(const u32x4*)(abase + gs * 64);
                 const bool first = F::AFF && (ls % F::WS == 0);
-                if constexpr (F::AFF) dsum = mfma_bf16(av, ones, first ? zero4 : dsum);
+                if constexpr (F::AFF && !XS) dsum = mfma_bf16(av, ones, first ? zero4 : dsum);
                 float sc = 0.f;
                 if constexpr (!F::AFF) {
                     int byte;
@@ -460,8 +507,11 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
                         const float zz = __builtin_fmaf(-F::OFF, s, z);
 #pragma unroll
                         for (int rr = 0; rr < MREG; ++rr) {
+                            float xs;
+                            if constexpr (XS) xs = xgroup_sum(rr, gw);
+                            else xs = dsum[rr];
                             ysum[rr] = __builtin_fmaf(s, acc[rr], ysum[rr]);
-                            ysum[rr] = __builtin_fmaf(zz, dsum[rr], ysum[rr]);
+                            ysum[rr] = __builtin_fmaf(zz, xs, ysum[rr]);
                         }
                     }
                 }
@@ -561,9 +611,12 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
         kern<<<blocks, threads, shm, st>>>(a);
         return hipGetLastError();
     };
-    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX>);
-    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX>);
-    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX>);
+    // group sums of x instead of the all-ones MFMA: affine, one row slot, M <= 4
+    constexpr bool XSOK = Fmt<MODE, BITS, G>::AFF && Fmt<MODE, BITS, G>::S == 1 && !DX;
+    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX, XSOK>);
+    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX, XSOK>);
+    if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, XSOK>);
+    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, false>);
 }
 
 template <int MODE, int BITS, int G, bool DX>

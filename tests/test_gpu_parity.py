@@ -168,12 +168,26 @@ def test_tiny_affine_config():
     assert normwise_rel_err(y, yref) <= 1e-5 * np.sqrt(512)
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("bits,g", AFFINE_CASES)
 def test_decode_kernel_affine(M, bits, g):
     if bits == 2 and g == 32 and M > 8:
         pytest.skip("2-bit g32 decode kernel takes M <= 8 (other paths cover it)")
     run_qmm_case(M, 80, 1024, bits, g, "affine", "bf16", True, path="decode", wid=21 + bits)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("K", [256, 3072, 8192])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_decode_kernel_x_group_sums(M, K, bits, g):
+    """Up to 4 rows the affine decode kernel sums x per group once (lane
+    reductions) instead of a second MFMA: slices of 1-8 groups, 2-16 lanes per
+    group, one or several rows per chunk register."""
+    if K % (8 * g) or K % (16 * 32 // bits):
+        pytest.skip("shape outside the decode kernel's rules")
+    if bits == 2 and g == 32:
+        pytest.skip("2-bit g32 keeps the MFMA sums (two row slots)")
+    run_qmm_case(M, 40, K, bits, g, "affine", "bf16", True, path="decode", wid=24 + bits)
 
 
 @pytest.mark.parametrize("M", [1, 5, 16])
