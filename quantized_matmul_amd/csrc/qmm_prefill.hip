@@ -108,6 +108,26 @@ __device__ __forceinline__ Chunk<WORDS> load_chunk(__amdgpu_buffer_rsrc_t r, uin
     return c;
 }
 
+// NB bytes (1, 2, 4, 8 or 16) at voff + soff, in BD = max(1, NB/4) dwords.
+template <int NB, int BD = (NB < 4 ? 1 : NB / 4)>
+__device__ __forceinline__ void load_bytes(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
+                                           uint32_t (&d)[BD]) {
+    if constexpr (NB == 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    } else if constexpr (NB == 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, soff, 0);
+        d[0] = v.x; d[1] = v.y;
+    } else if constexpr (NB == 4) {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, soff, 0);
+    } else if constexpr (NB == 2) {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, soff, 0);
+    } else {
+        static_assert(NB == 1, "1, 2, 4, 8 or 16 bytes");
+        d[0] = __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, soff, 0);
+    }
+}
+
 // Dequantize CPC codes (natural k order) into CPC/2 packed bf16 pairs.
 // Affine: bf16(fmaf(s, q, z)), the dequantized value rounded once to the
 // MFMA input type. Microscaled: exact decode times the group scale.
@@ -175,14 +195,13 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     constexpr int RCH = (NCH % NTH == 0 && NCH / NTH <= CROW && CROW % (NCH / NTH) == 0) ? NCH / NTH : 1;
     constexpr int CPT = RCH > 1 ? 1 : (NCH + NTH - 1) / NTH;   // runs (or chunks) per thread
     constexpr int RWORDS = RCH * WORDS;               // packed dwords per run
-    constexpr int NGT = (RCH * CPC + G - 1) / G;      // groups a run spans (1 or 2)
-    static_assert(NGT <= 2 && (NGT == 1 || RCH * CPC == 2 * G), "a run spans one or two whole groups");
     constexpr int MW = BM / WM, NW = BN / WN;         // wave tile
     constexpr int MT = MW / 16, NT = NW / 16;
     static_assert(WORDS >= 1 && G % CPC == 0, "a chunk lies inside one group");
     static_assert(MW % 16 == 0 && NW % 16 == 0, "wave tile is a multiple of the MFMA tile");
     constexpr int NWV = WM * WN;
-    constexpr int XST = 3, XSTAGE = BM * BK * 2, WSTAGE = BN * LROW;
+    // activations are loaded XLA = 2 steps ahead into XST = 3 LDS stages
+    constexpr int XLA = 2, XST = XLA + 1, XSTAGE = BM * BK * 2, WSTAGE = BN * LROW;
     constexpr int XDMA = BM * 8 / NTH;                 // activation loads per thread per step
     static_assert(XDMA * NTH == BM * 8, "activation tile splits into whole wave loads");
 
@@ -279,7 +298,8 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     // scale (and bias) load of the groups they span. Otherwise chunk
     // c = tid + p*NTH -> weight row c / CROW, chunk c % CROW; spare slots of an
     // uneven split reload the last chunk and skip the store.
-    uint32_t woff[CPT], goff[CPT], ldsoff[CPT];
+    uint32_t woff[CPT], rowg[CPT], ldsoff[CPT];
+    int ccv[CPT];
     bool cact[CPT];
 #pragma unroll
     for (int p = 0; p < CPT; ++p) {
@@ -299,50 +319,60 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         // their outputs are never stored
         const uint32_t n = (uint32_t)expert * (uint32_t)a.N + (uint32_t)(n0 + r);
         woff[p] = (n * (K / PER) + (uint32_t)cc * WORDS) * 4u;
-        goff[p] = n * ngroups + (uint32_t)(cc * CPC) / G;   // + kt * BK / G
+        rowg[p] = n * ngroups * SB;                         // first scale byte of the row
+        ccv[p] = cc;
         ldsoff[p] = (uint32_t)r * LROW + (uint32_t)cc * CPC * 2u;
     }
-    // scale / bias bits stay raw until the dequant step, so nothing waits
-    // on these loads before they are needed
-    auto load_w = [&](Chunk<RWORDS> (&dst)[CPT], uint32_t (&ds)[CPT], uint32_t (&dz)[CPT], int kt) {
+    // Scales and biases: one load per weight row for a batch of WPF steps
+    // (the groups those steps cover, NBB bytes), instead of one small load per
+    // chunk and step: the lanes of a row share one request. Batch b covers
+    // steps [b * WPF, (b + 1) * WPF); the host picks WPF dividing the step
+    // count, so a batch is NBB-aligned in every row. Bits stay raw until the
+    // dequant step, so nothing waits on these loads before they are needed.
+    constexpr bool WHOLE = (WPF * BK) % G == 0;         // a batch covers whole groups
+    constexpr int NGB = WHOLE ? WPF * BK / G : 1;       // groups per batch
+    constexpr int NBB = NGB * (int)SB;                  // bytes per batch and row
+    constexpr int BD = NBB < 4 ? 1 : NBB / 4;           // dwords per batch and row
+    static_assert(NBB <= 16, "a batch is at most 16 bytes per row");
+    auto load_codes = [&](Chunk<RWORDS> (&dst)[CPT], int kt) {
+#pragma unroll
+        for (int p = 0; p < CPT; ++p) dst[p] = load_chunk<RWORDS>(wr, woff[p], kt * (BK / PER) * 4);
+    };
+    auto load_batch = [&](uint32_t (&ds)[CPT][BD], uint32_t (&dz)[CPT][BD], int kt0) {
+        const int first = (kt0 * BK) / G;  // first group of the batch (scalar)
 #pragma unroll
         for (int p = 0; p < CPT; ++p) {
-            dst[p] = load_chunk<RWORDS>(wr, woff[p], kt * (BK / PER) * 4);
-            const int gk = kt * BK / G;  // group of the step (scalar)
-            if constexpr (MODE == AFFINE) {
-                // one 2-byte value per group spanned (NGT = 1 or 2)
-                if constexpr (NGT == 1) {
-                    ds[p] = __builtin_amdgcn_raw_buffer_load_b16(sr, (int)(goff[p] * 2u), gk * 2, 0);
-                    dz[p] = __builtin_amdgcn_raw_buffer_load_b16(br, (int)(goff[p] * 2u), gk * 2, 0);
-                } else {
-                    ds[p] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)(goff[p] * 2u), gk * 2, 0);
-                    dz[p] = __builtin_amdgcn_raw_buffer_load_b32(br, (int)(goff[p] * 2u), gk * 2, 0);
-                }
-            } else {
-                if constexpr (NGT == 1)
-                    ds[p] = __builtin_amdgcn_raw_buffer_load_b8(sr, (int)goff[p], gk, 0);
-                else
-                    ds[p] = __builtin_amdgcn_raw_buffer_load_b16(sr, (int)goff[p], gk, 0);
-                dz[p] = 0u;
-            }
+            load_bytes<NBB>(sr, rowg[p], first * (int)SB, ds[p]);
+            if constexpr (MODE == AFFINE) load_bytes<NBB>(br, rowg[p], first * (int)SB, dz[p]);
         }
     };
-    auto store_w = [&](unsigned char* base, const Chunk<RWORDS> (&wc)[CPT], const uint32_t (&sc)[CPT],
-                       const uint32_t (&zc)[CPT]) {
+    // t: the step's place in its batch (compile time). The group of chunk
+    // (p, h) is (t * BK + k) / G within the batch, k its offset in the step;
+    // a step's scale bytes never straddle a dword, so the dword is known at
+    // compile time and only the byte shift depends on the lane.
+    auto store_w = [&](unsigned char* base, const Chunk<RWORDS> (&wc)[CPT], const uint32_t (&sc)[CPT][BD],
+                       const uint32_t (&zc)[CPT][BD], auto tc) {
+        constexpr int T = decltype(tc)::value;
+        constexpr int DW = WHOLE ? (((T * BK) / G) * (int)SB) / 4 : 0;
+        static_assert(DW < BD, "batch dword");
 #pragma unroll
         for (int p = 0; p < CPT; ++p) {
             if (RCH == 1 && NCH % NTH != 0 && !cact[p]) continue;
 #pragma unroll
             for (int h = 0; h < RCH; ++h) {
-                // group of chunk h within the run
-                constexpr int CPG = G / CPC > 0 ? G / CPC : 1;   // chunks per group
-                const int gsel = NGT == 1 ? 0 : h / CPG;
+                int sh = 0;
+                if constexpr (WHOLE && G >= BK) {
+                    sh = 8 * ((((T * BK) / G) * (int)SB) & 3);
+                } else if constexpr (WHOLE) {
+                    const int byte = ((T * BK + (ccv[p] + h) * CPC) / G) * (int)SB;
+                    sh = 8 * (byte - 4 * DW);
+                }
                 float sf, zf;
                 if constexpr (MODE == AFFINE) {
-                    sf = bf16_bits_to_f32((sc[p] >> (16 * gsel)) & 0xFFFFu);
-                    zf = bf16_bits_to_f32((zc[p] >> (16 * gsel)) & 0xFFFFu);
+                    sf = bf16_bits_to_f32((sc[p][DW] >> sh) & 0xFFFFu);
+                    zf = bf16_bits_to_f32((zc[p][DW] >> sh) & 0xFFFFu);
                 } else {
-                    const uint32_t byte = (sc[p] >> (8 * gsel)) & 0xFFu;
+                    const uint32_t byte = (sc[p][DW] >> sh) & 0xFFu;
                     sf = MODE == NVFP4 ? e4m3_to_f32(byte) : e8m0_to_f32(byte);
                     zf = 0.f;
                 }
@@ -370,42 +400,59 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     // u % WPF belongs to step u. The step loop is unrolled WPF times so set
     // indices are compile-time.
     Chunk<RWORDS> wset[WPF][CPT];
-    uint32_t sset[WPF][CPT], zset[WPF][CPT];
+    // scale/bias batches: the current one (steps kt0 .. kt0+WPF-1) and the next
+    uint32_t scur[CPT][BD], zcur[CPT][BD], snxt[CPT][BD], znxt[CPT][BD];
     unsigned char* const wbuf = smem + XST * XSTAGE;
 
-    // prologue: activations of steps 0 and 1 in flight, codes of steps
-    // 0 .. WPF-1 in flight, step 0's weights dequantized into buffer 0
-    dma_x(0, 0);
-    load_w(wset[0], sset[0], zset[0], 0);
-    dma_x(1, nk > 1 ? 1 : 0);
-    unroll<1, WPF>([&](auto u) {
+    // prologue: activations of steps 0 and 1 and codes of steps 0 .. WPF-1
+    // in flight, step by step, each step's activation loads first (the
+    // scheduling barriers keep that order: the waits below count on it);
+    // step 0's weights dequantized into buffer 0
+    constexpr int PRO = XLA > WPF ? XLA : WPF;
+    unroll<0, PRO>([&](auto u) {
         constexpr int U = decltype(u)::value;
-        load_w(wset[U], sset[U], zset[U], U < nk ? U : nk - 1);
+        if constexpr (U < XLA) dma_x(U, U < nk ? U : nk - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (U < WPF) load_codes(wset[U], U < nk ? U : nk - 1);
+        if constexpr (U == 0) load_batch(scur, zcur, 0);
+        __builtin_amdgcn_sched_barrier(0);
     });
-    store_w(wbuf, wset[0], sset[0], zset[0]);  // waits for step 0's codes, hence its activations
+    // waits for step 0's codes, issued after its activations
+    store_w(wbuf, wset[0], scur, zcur, std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes done
     asm volatile("s_barrier" ::: "memory");
 
     // One step. Activation loads issued here land two steps later, code
     // loads WPF steps later. vm operations complete in order; at the end of
-    // step kt the activations of step kt+1 (issued at step kt-1) must be in
-    // LDS, so the wait leaves outstanding only what was issued after them:
-    // the code loads of step kt-1 and this step's loads. The step ends with
-    // that wait, lgkmcnt(0) (this wave's LDS writes done) and a plain
+    // step kt the activations of step kt+1 (issued first in step kt-1, or in
+    // the prologue) must be in LDS, so the wait may leave outstanding only
+    // loads issued after them: step kt-1's code loads (and its batch of
+    // scales and biases when it opened a batch) and all of step kt's loads.
+    // With one step per batch (WPF = 1) only step kt's loads are counted
+    // (the prologue issues nothing after step 1's activations). The step ends
+    // with that wait, lgkmcnt(0) (this wave's LDS writes done) and a plain
     // s_barrier: a fenced barrier would also wait for this step's loads.
-    // code and scale loads per step (a 32-byte run takes two loads)
-    constexpr int WL = CPT * ((RWORDS == 8 ? 2 : 1) + (MODE == AFFINE ? 2 : 1));
-    constexpr int VM_ALLOWED = XDMA + WL + (WPF > 2 ? WL : 0);
-    static_assert(VM_ALLOWED < 64, "vmcnt range");
-    // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-    constexpr int WAIT_IMM = (VM_ALLOWED & 15) | (7 << 4) | (0 << 8) | ((VM_ALLOWED >> 4) << 14);
+    constexpr int WL = CPT * (RWORDS == 8 ? 2 : 1);            // code loads per step
+    constexpr int BL = CPT * (MODE == AFFINE ? 2 : 1);         // batch loads (steps U = 0)
+    auto wait_imm = [](int U) constexpr {
+        int vm = XDMA + WL + (U == 0 ? BL : 0);                // this step
+        if (WPF > 1) vm += WL + (U == 1 ? BL : 0);             // step kt-1 after its activations
+        // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+        return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14);
+    };
+    static_assert(XDMA + 2 * WL + 2 * BL < 64, "vmcnt range");
     auto step = [&](int kt, auto uc) {
         constexpr int U = decltype(uc)::value;          // kt % WPF
         constexpr int CUR = (U + 1) % WPF;              // set of step kt+1 (dequantized now)
-        const int kx = kt + 2 < nk ? kt + 2 : nk - 1;
+        const int kx = kt + XLA < nk ? kt + XLA : nk - 1;
         const int kw = kt + WPF < nk ? kt + WPF : nk - 1;
-        dma_x((kt + 2) % XST, kx);
-        load_w(wset[U], sset[U], zset[U], kw);          // set U held step kt, dequantized last step
+        dma_x((kt + XLA) % XST, kx);
+        __builtin_amdgcn_sched_barrier(0);              // activations first (the wait counts on it)
+        load_codes(wset[U], kw);                        // set U held step kt, dequantized last step
+        if constexpr (U == 0) {
+            // the next batch (steps kt+WPF .. kt+2*WPF-1; past the end: the last batch)
+            load_batch(snxt, znxt, kt + WPF < nk ? kt + WPF : nk - WPF);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* xt = smem + (kt % XST) * XSTAGE;
         const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
@@ -428,15 +475,30 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         // step kt+1's weights (beyond the last step this fills an unused
         // buffer), dequantized between the two halves of this step's MFMAs
         mma(0, 1);
-        store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wset[CUR], sset[CUR], zset[CUR]);
+        // step kt+1 is the next batch's first step when U is the last place
+        if constexpr (U + 1 < WPF)
+            store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wset[CUR], scur, zcur,
+                    std::integral_constant<int, U + 1>{});
+        else
+            store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wset[CUR], snxt, znxt,
+                    std::integral_constant<int, 0>{});
         mma(1, 2);
+        constexpr int WAIT_IMM = wait_imm(U);
         __builtin_amdgcn_s_waitcnt(WAIT_IMM);
         asm volatile("s_barrier" ::: "memory");
     };
     // the host picks WPF dividing the step count, so every unrolled step runs
     // (a conditional step would blur the compiler's load-count bookkeeping)
-    for (int kt = 0; kt < nk; kt += WPF)
+    for (int kt = 0; kt < nk; kt += WPF) {
         unroll<0, WPF>([&](auto u) { step(kt + decltype(u)::value, u); });
+#pragma unroll
+        for (int p = 0; p < CPT; ++p)
+#pragma unroll
+            for (int d = 0; d < BD; ++d) {
+                scur[p][d] = snxt[p][d];
+                zcur[p][d] = znxt[p][d];
+            }
+    }
 
     // ---- epilogue: lane holds D[n = 4j + r][m = i] of each (t, s) tile
 #pragma unroll
@@ -463,18 +525,24 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
 }
 
 #ifndef QLIN_PREFILL_WPF
-#define QLIN_PREFILL_WPF 2
+#define QLIN_PREFILL_WPF 4
 #endif
 #ifndef QLIN_GATHER_WPF
 #define QLIN_GATHER_WPF 4
 #endif
 
+
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, bool GATHER>
 hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     // a chunk holds at least one packed dword
     constexpr int CPC = CPC0 < 32 / BITS ? 32 / BITS : CPC0;
-    constexpr int WPF = GATHER ? QLIN_GATHER_WPF : QLIN_PREFILL_WPF;
+    // the plain tile keeps 4-step batches of scales only where they fit 8
+    // bytes per row (16-byte batches of two sets push its registers over)
+    constexpr int SBY = MODE == AFFINE ? 2 : 1;
+    constexpr int B4 = (4 * BK / G > 0 ? 4 * BK / G : 1) * SBY;
+    constexpr int WPF = GATHER ? QLIN_GATHER_WPF : (B4 <= 8 ? QLIN_PREFILL_WPF : 2);
     const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
+    static_assert(3 * BM * BK * 2 + 2 * BN * LROW <= 160 * 1024, "LDS budget");
     auto run = [&](auto kern) -> hipError_t {
         static bool attr_set = false;  // per instantiation, host side
         if (!attr_set) {
@@ -620,6 +688,9 @@ hipError_t launch_tag(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
 
 bool qmm_prefill_supports(const QmmArgs& q) {
     if (!q.transpose || q.x_dtype != QLIN_BF16) return false;
+    // scales and biases are read in batches of up to 16 bytes per row
+    if (((uintptr_t)q.scales & 15) != 0) return false;
+    if (q.mode == AFFINE && ((uintptr_t)q.biases & 15) != 0) return false;
     if (q.K % BK != 0 || q.M < 1) return false;
     if (q.R > 0 && (q.E > 8192 || q.R * q.M >= (1LL << 30))) return false;
     // 32-bit buffer offsets over x, the (stacked) weight and its scales
