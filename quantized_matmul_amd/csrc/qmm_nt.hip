@@ -13,8 +13,10 @@
 //     columns and the grid has enough workgroups; its 16 waves split K and
 //     meet once in LDS; the weight words stream through a 16-deep prefetch
 //     ring;
-//   * x and the workgroup's scale/bias columns for all of K are staged in
-//     LDS up front (loads all issued before any use).
+//   * x for all of K is staged in LDS up front; each row's scale and bias
+//     ride in the prefetch ring with its packed word (staging them up front
+//     serialised thousands of scattered 2-byte loads before the weight
+//     stream started: 27 -> 25 us at M1, 63 -> 53 us at M8).
 
 #include "qlin_common.h"
 
@@ -35,18 +37,18 @@ struct NtArgs {
 // Lane (rr, cl) = (lane / WPB, lane % WPB) handles packed word c0 + cl of
 // row k = RPS * step + rr: one wave load covers RPS = 64 / WPB rows x WPB
 // words. The NW waves of a workgroup split K. Each lane keeps RING2 steps
-// (word, scale, bias) in flight. MR = activation rows rounded up (<= 8).
-constexpr int RING2 = 16; // steps in flight per lane
-
+// (word, scale, bias) in flight: 16 for up to 2 activation rows of affine
+// codes, fewer otherwise (the accumulators and decoding take the
+// registers). MR = activation rows rounded up (<= 8).
 template <int MODE, int BITS, int G, int MR, int WPB, int NW>
 __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
+    // steps in flight per lane (microscaled decoding needs more registers)
+    constexpr int RING2 = (MR <= 2 && MODE == AFFINE) ? 16 : (MR <= 4 ? 8 : 4);
     constexpr int NWAVES = NW;
     constexpr int RPS = 64 / WPB;                     // rows per step
     constexpr int PER = 32 / BITS;
     constexpr bool AFF = MODE == AFFINE;
     constexpr int SBYTES = AFF ? 2 : 1;               // bytes per scale value
-    // groups spanned by the workgroup's WPB words (its columns are aligned)
-    constexpr int GW = (WPB * PER) >= G ? (WPB * PER) / G : 1;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rr = lane / WPB, cl = lane % WPB;
@@ -65,12 +67,10 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     const int g0 = (cb * WPB * PER) / G;              // first group of the workgroup
     const int gl = active ? (c * PER) / G - g0 : 0;   // the lane's group, local
 
-    // LDS: x [MR][K] bf16 | scales [K][GW] | biases [K][GW]
+    // LDS: x [MR][K] bf16
     uint16_t* xs = (uint16_t*)smem;
-    unsigned char* ss = smem + (size_t)MR * K * 2;
-    unsigned char* zs = ss + (size_t)K * GW * SBYTES;
 
-    // ---- stage x, scales and biases with loads all issued before any use
+    // ---- stage x with loads all issued before any use
     {
         const uint16_t* xg = a.x;
         const int xv8 = (a.M * K) / 8;                // 16-byte chunks of x (K % 8 == 0)
@@ -86,45 +86,6 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
             for (int t = 0; t < XI; ++t) {
                 const int idx = base + t * 64 * NW + tid;
                 if (idx < MR * K / 8) *(u32x4*)(xs + (size_t)idx * 8) = v[t];
-            }
-        }
-        // scale/bias rows: GW values per row, rows spread over the threads;
-        // all loads of a round are issued before its stores
-        const int ngl = min(GW, gpr - g0);            // groups that exist
-        constexpr int KT = 8;                          // rows per thread per round
-        for (int kb0 = 0; kb0 < K; kb0 += KT * 64 * NW) {
-            uint32_t sv[KT][GW], zv[KT][GW];
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                const int k = kb0 + t * 64 * NW + tid;
-                const int kc = k < K ? k : K - 1;
-                const size_t gi = (size_t)kc * gpr + g0;
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    const int gg = g < ngl ? g : 0;
-                    if constexpr (AFF) {
-                        sv[t][g] = ((const uint16_t*)a.scales)[gi + gg];
-                        zv[t][g] = a.biases[gi + gg];
-                    } else {
-                        sv[t][g] = ((const uint8_t*)a.scales)[gi + gg];
-                        zv[t][g] = 0u;
-                    }
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                const int k = kb0 + t * 64 * NW + tid;
-                if (k < K) {
-#pragma unroll
-                    for (int g = 0; g < GW; ++g) {
-                        if constexpr (AFF) {
-                            ((uint16_t*)ss)[k * GW + g] = (uint16_t)sv[t][g];
-                            ((uint16_t*)zs)[k * GW + g] = (uint16_t)zv[t][g];
-                        } else {
-                            ss[k * GW + g] = (uint8_t)sv[t][g];
-                        }
-                    }
-                }
             }
         }
     }
@@ -147,11 +108,25 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     }
 
     const uint32_t* wp = a.wq + (active ? c : 0);
-    uint32_t rw[RING2];
+    uint32_t rw[RING2], rs[RING2], rz[RING2];
+    const uint32_t sbytes_all = (uint32_t)K * (uint32_t)gpr * SBYTES;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.scales), (short)0, (int)sbytes_all, 0x00020000);
+    const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(AFF ? a.biases : (const uint16_t*)a.scales), (short)0,
+        (int)(AFF ? sbytes_all : 0u), 0x00020000);
+    const uint32_t gcol = (uint32_t)(g0 + gl);  // the lane's group column
     auto fetch = [&](int slot, int st) {
         const int k = RPS * st + rr;
         const int kk = (active && k < K) ? k : 0;
         rw[slot] = wp[(size_t)kk * wcols];
+        const uint32_t so = ((uint32_t)kk * (uint32_t)gpr + gcol) * (uint32_t)SBYTES;
+        if constexpr (AFF) {
+            rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)so, 0, 0);
+            rz[slot] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)so, 0, 0);
+        } else {
+            rs[slot] = __builtin_amdgcn_raw_buffer_load_b8(srs, (int)so, 0, 0);
+        }
     };
     auto consume = [&](int slot, int st) {
         const uint32_t w = rw[slot];
@@ -160,10 +135,10 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
         const int k = ok ? kr : 0;
         float s, z = 0.f;
         if constexpr (AFF) {
-            s = bf16_bits_to_f32(((const uint16_t*)ss)[k * GW + gl]);
-            z = bf16_bits_to_f32(((const uint16_t*)zs)[k * GW + gl]);
+            s = bf16_bits_to_f32(rs[slot] & 0xFFFFu);
+            z = bf16_bits_to_f32(rz[slot] & 0xFFFFu);
         } else {
-            const uint32_t b = ss[k * GW + gl];
+            const uint32_t b = rs[slot] & 0xFFu;
             s = MODE == NVFP4 ? e4m3_to_f32(b) : e8m0_to_f32(b);
         }
         s = ok ? s : 0.f;
@@ -258,11 +233,10 @@ inline int nt_mr(int M) { return M <= 2 ? M : (M <= 4 ? 4 : 8); }
 // register ring then holds more accumulators per lane)
 inline int nt_waves(int M) { return nt_mr(M) == 8 ? 8 : QLIN_NT_NW; }
 
-inline size_t nt_shm(int M, int K, int per, int G, bool aff) {
+inline size_t nt_shm(int M, int K, int per) {
     const int wpb = QLIN_NT_WPB;
-    const int gw = (wpb * per) >= G ? (wpb * per) / G : 1;
     const size_t red_bytes = (size_t)nt_waves(M) * wpb * per * 4;
-    const size_t stage = (size_t)nt_mr(M) * K * 2 + (size_t)K * gw * (aff ? 4 : 1);
+    const size_t stage = (size_t)nt_mr(M) * K * 2;
     return stage > red_bytes ? stage : red_bytes;
 }
 
@@ -281,7 +255,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     const int wcols = a.N / PER;
     constexpr int WPB = QLIN_NT_WPB, NW = QLIN_NT_NW;
     const unsigned blocks = (unsigned)((wcols + WPB - 1) / WPB);
-    const size_t shm = nt_shm(a.M, a.K, PER, G, MODE == AFFINE);
+    const size_t shm = nt_shm(a.M, a.K, PER);
     auto run = [&](auto kern, int nw) -> hipError_t {
         if (shm > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -306,7 +280,7 @@ bool qmm_nt_supports(const QmmArgs& q) {
     if (q.M < 1 || q.M > 8) return false;
     if (q.K > (1 << 20) || q.N > (1 << 28)) return false;
     if (q.K % 8 != 0 || ((uintptr_t)q.x & 15) != 0) return false;
-    return nt_shm((int)q.M, (int)q.K, 32 / q.bits, q.group_size, q.mode == AFFINE) <= 150 * 1024;
+    return nt_shm((int)q.M, (int)q.K, 32 / q.bits) <= 150 * 1024;
 }
 
 hipError_t launch_qmm_nt(const QmmArgs& q, hipStream_t st) {

@@ -260,6 +260,29 @@ def test_nt_kernel_micro(M, mode, g, bits):
     run_qmm_case(M, 768, 256, bits, g, mode, "bf16", False, path="decode", wid=82)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 4160), (2, 3072, 1000), (3, 640, 2048), (5, 512, 64),
+                                   (8, 1536, 8)])
+@pytest.mark.parametrize("bits,g", [(4, 64), (8, 32), (2, 128)])
+def test_nt_kernel_k_slices(M, N, K, bits, g):
+    """[in, out] layout: K not a multiple of the waves' slices (ragged last
+    slice), K shorter than one prefetch ring, a single row of K."""
+    if N % g:
+        pytest.skip("group does not divide N")
+    run_qmm_case(M, N, K, bits, g, "affine", "bf16", False, path="decode", wid=84 + bits)
+
+
+def test_nt_kernel_repeat_is_deterministic():
+    """Partial sums meet in a fixed order: repeated calls agree bit for bit."""
+    w, _ = gpu_weight((4096, 2048), 0.02, 86, "bf16")
+    qw = qm.quantize(w, 64, 4, "affine", transpose=False)
+    x, _ = synth.normal((3, 4096), 1.0, 86, synth.ACT, "bf16")
+    x = x.to(DEV)
+    ys = [qm.quantized_matmul(x, qw) for _ in range(4)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
 @pytest.mark.parametrize("transpose", [True, False])
 @pytest.mark.parametrize("xdtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("bits,g", [(2, 32), (4, 64), (8, 128)])
