@@ -50,6 +50,7 @@ struct PrefillArgs {
     const uint32_t* offsets;  // [E+1] index-row offset of each expert
     const uint32_t* tiles;    // [E+1] row-tile prefix of each expert
     int E, B;
+    int xgm;                  // plain form: the 8 XCDs as an xgm x (8/xgm) grid of tile blocks (0: rows)
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -232,13 +233,24 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         row_begin = (int)a.offsets[lo];
         row_count = ((int)a.offsets[lo + 1] - row_begin) * a.M;
     } else {
-        // blocks are dealt to the 8 XCDs round-robin; renumber so that each
-        // XCD walks a contiguous run of tiles along N
+        // Blocks are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8).
+        // With xgm > 0 the host has split the tile grid into xgm x (8/xgm)
+        // equal blocks, one per XCD, so an XCD's L2 fetches only its block's
+        // share of x and W (each XCD walking a row of tiles fetched all of
+        // W); otherwise each XCD walks a contiguous run of tiles along N.
         int b = blockIdx.x;
         const int nblk = gridDim.x;
-        if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
-        m0 = (b / ntn) * BM;
-        n0 = (b % ntn) * BN;
+        if (a.xgm > 0) {
+            const int xgn = 8 / a.xgm, ntm = (a.M + BM - 1) / BM;
+            const int mt = ntm / a.xgm, nt = ntn / xgn;      // tiles per XCD block
+            const int x = b & 7, j = b >> 3;
+            m0 = ((x / xgn) * mt + j / nt) * BM;
+            n0 = ((x % xgn) * nt + j % nt) * BN;
+        } else {
+            if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
+            m0 = (b / ntn) * BM;
+            n0 = (b % ntn) * BN;
+        }
     }
     // GEMM row rho of the tile's problem -> index row (gather) / x row / y row
     auto x_row = [&](int rho) -> uint32_t {
@@ -561,9 +573,34 @@ hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 1>);
 }
 
+// XCD grid for the plain form: the 8 XCDs take an xgm x (8/xgm) grid of
+// equal tile blocks; xgm minimises what the XCDs fetch in all, xgm copies of
+// the weight plus 8/xgm copies of x (0: the tile grid does not split evenly).
+inline int xcd_grid_rows(int64_t ntm, int64_t ntn, double w_bytes, double x_bytes) {
+#ifdef QLIN_PREFILL_XCD_ROWS
+    return 0;
+#endif
+    int best = 0;
+    double best_cost = 0;
+    for (int gm = 1; gm <= 8; gm <<= 1) {
+        const int gn = 8 / gm;
+        if (ntm % gm || ntn % gn) continue;
+        const double cost = gm * w_bytes + gn * x_bytes;
+        if (best == 0 || cost < best_cost) {
+            best = gm;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0>
-hipError_t launch_plain(const PrefillArgs& t, hipStream_t st) {
-    const int grid = ((t.M + BM - 1) / BM) * ((t.N + BN - 1) / BN);
+hipError_t launch_plain(const PrefillArgs& t0, hipStream_t st) {
+    PrefillArgs t = t0;
+    const int64_t ntm = (t.M + BM - 1) / BM, ntn = (t.N + BN - 1) / BN;
+    const double w_bytes = (double)t.N * t.K * BITS / 8.0, x_bytes = (double)t.M * t.K * 2.0;
+    t.xgm = xcd_grid_rows(ntm, ntn, w_bytes, x_bytes);
+    const int grid = (int)(ntm * ntn);
     return launch_cfg<MODE, BITS, G, BM, BN, WM, WN, CPC0, false>(t, grid, st);
 }
 
