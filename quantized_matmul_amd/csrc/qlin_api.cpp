@@ -253,18 +253,26 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
     a.rhs = rhs_indices;
     hipStream_t s = (hipStream_t)stream;
     uint32_t *perm = nullptr, *offsets = nullptr;
-    // the MFMA paths read rows bucketed by expert, in tiles of their own size
+    // the MFMA paths read rows bucketed by expert, in tiles of their own size;
+    // few rows per expert (decode) take the small-M kernel's gather form
     const int force = forced_path();
-    int tile_rows = 0;
-    if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
+    int tile_rows = 0, decode_rows = 0;
+    if ((force == 0 || force == 2) && (decode_rows = qlin::qmm_decode_gather_tile_rows(a)) != 0)
+        tile_rows = decode_rows;   // -1: no bucketing
+    else if (force == 2)
+        return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this gather shape");
+    else if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
         tile_rows = qlin::kPrefillGatherRows;
     else if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
         tile_rows = qlin::kTiledGatherRows;
-    if (tile_rows) {
+    if (tile_rows > 0) {
         hipError_t e = qlin::launch_bucket(rhs_indices, R, E, M, sorted_indices, tile_rows,
                                            workspace, &perm, &offsets, s);
         if (e != hipSuccess) return device_status(e, "gather_qmm (expert bucketing)");
     }
+    if (decode_rows != 0)
+        return device_status(qlin::launch_qmm_decode_gather(a, perm, offsets, decode_rows, s),
+                             "gather_qmm (decode kernel)");
     return run_qmm(a, perm, offsets, s);
 }
 

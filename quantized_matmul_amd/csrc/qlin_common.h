@@ -130,6 +130,13 @@ bool qmm_prefill_supports(const QmmArgs& a);
 hipError_t launch_qmm_nt(const QmmArgs& a, hipStream_t s);
 bool qmm_nt_supports(const QmmArgs& a);
 bool qmm_decode_supports(const QmmArgs& a);
+// Gather form of the small-M kernel (transpose, bf16 x, few rows per
+// expert): rows bucketed by expert into tiles of the returned height, each
+// tile streaming its expert's weight once; -1: far fewer rows than experts,
+// each index row is its own tile and no bucketing is needed; 0: not taken.
+int qmm_decode_gather_tile_rows(const QmmArgs& a);
+hipError_t launch_qmm_decode_gather(const QmmArgs& a, const uint32_t* row_perm,
+                                    const uint32_t* expert_offsets, int tile_rows, hipStream_t s);
 // MoE bucketing: counts rows per expert, scans, and writes the stable
 // permutation of rows sorted by expert (skipped when rows are pre-sorted).
 // rows_per_tile sets the row-tile prefix written after the offsets.

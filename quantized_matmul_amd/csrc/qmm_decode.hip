@@ -179,8 +179,17 @@ struct DecodeArgs {
     const void* scales;  // bf16 [N, K/G] (affine) or u8
     const uint16_t* biases;
     uint16_t* y;         // bf16 [M, N]
-    int M, N, K;
+    int M, N, K;         // gather: M = GEMM rows per row tile (the tile height)
     int cols;            // output columns per workgroup (<= 16, the MFMA width)
+    // gather form (GATHER kernels), wq/scales/biases stacking E experts:
+    // bucketed (perm != null): blockIdx.y is a row tile of one expert;
+    // direct (perm == null): blockIdx.y is index row r, expert rhs[r]
+    const uint32_t* perm;     // [R] index rows in expert order
+    const uint32_t* offsets;  // [E+1] index-row offset of each expert
+    const uint32_t* tiles;    // [E+1] row-tile prefix of each expert
+    const uint32_t* rhs;      // [R] expert of each index row (direct form)
+    const uint32_t* lhs;      // [R] x batch entry of each index row, or null (identity)
+    int E, Mx, R, xrows;      // experts; x rows per index row; index rows; rows of x
 };
 
 // LDS layout: (M+1) rows of K/8 16-byte chunks (row M is zero), each row
@@ -249,11 +258,18 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 // its A fragments from global memory together with the weight unit they
 // multiply; x of any size then fits one launch (the LDS keeps only the
 // cross-wave sums).
-template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS>
+// GATHER (staged path only): blockIdx.y is a row tile of one expert
+// (bucketed rows, tile height a.M); the workgroup's weight, scales and biases
+// are that expert's, its x rows come through the row permutation and lhs,
+// and its y rows go back to the index rows' places. The index loads are
+// issued first, the weight stream next, and the x loads (which need them)
+// last, so the weight stream never waits on the index chain.
+template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER>
 __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
+    static_assert(!GATHER || !DX, "the gather form stages x in LDS");
     constexpr int KW = UPW * F::U;                 // k per wave
     extern __shared__ __align__(16) unsigned char smem[];
     const int KS = (int)(blockDim.x >> 6);
@@ -262,7 +278,44 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     // scalar offset operand, which must be provably wave-uniform
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 15, j = lane >> 4;
-    const int K = a.K, M = a.M;
+    const int K = a.K;
+    // rows of this workgroup's problem; gather: its tile of one expert
+    int M = a.M, m0 = 0, row_begin = 0;
+    const uint32_t* wqp = a.wq;
+    const unsigned char* scp = (const unsigned char*)a.scales;
+    const uint16_t* bip = a.biases;
+    if (GATHER && !a.perm) {
+        // direct form: one index row per tile
+        row_begin = blockIdx.y;
+        const int lo = (int)a.rhs[row_begin];
+        M = a.Mx;
+        const size_t erows = (size_t)lo * (size_t)a.N;   // stacked weight rows before expert lo
+        wqp += erows * (size_t)(K / F::PER);
+        scp += erows * (size_t)(K / G) * (F::AFF ? 2 : 1);
+        if constexpr (F::AFF) bip += erows * (size_t)(K / G);
+    } else if constexpr (GATHER) {
+        // the expert: tiles[] is non-decreasing from tiles[0] = 0, so the
+        // number of entries <= tile, less one, is the lo with tiles[lo] <=
+        // tile < tiles[lo + 1] (one load per lane per 64 entries and a
+        // ballot count instead of a chain of dependent loads)
+        const uint32_t tile = blockIdx.y;
+        int cnt = 0;
+        for (int b0 = 0; b0 <= a.E; b0 += 64) {
+            const int e = b0 + lane;
+            const uint32_t t = a.tiles[e <= a.E ? e : a.E];
+            cnt += __popcll(__ballot(e <= a.E && t <= tile));
+        }
+        if (cnt > a.E) return;                       // past the real tile count
+        const int lo = cnt - 1;
+        m0 = ((int)tile - (int)a.tiles[lo]) * a.M;
+        row_begin = (int)a.offsets[lo];
+        const int rows = ((int)a.offsets[lo + 1] - row_begin) * a.Mx;
+        M = min(a.M, rows - m0);
+        const size_t erows = (size_t)lo * (size_t)a.N;   // stacked weight rows before expert lo
+        wqp += erows * (size_t)(K / F::PER);
+        scp += erows * (size_t)(K / G) * (F::AFF ? 2 : 1);
+        if constexpr (F::AFF) bip += erows * (size_t)(K / G);
+    }
     const int rowb = xrow_bytes(K);
     float* red = (float*)(smem + (DX ? 0 : (M + 1) * rowb));  // [KS][16 rows][16 cols]
 
@@ -277,7 +330,7 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     const bool colv = i < a.cols && n0 + i < a.N;
     const uint32_t ncol = (uint32_t)(n0 + i);
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint32_t*>(a.wq), (short)0, (int)((uint32_t)a.N * (uint32_t)wpr * 4u), 0x00020000);
+        const_cast<uint32_t*>(wqp), (short)0, (int)((uint32_t)a.N * (uint32_t)wpr * 4u), 0x00020000);
     const uint32_t woff = colv ? (ncol * (uint32_t)wpr + 4u * j) * 4u : 0x80000000u;
     auto wload = [&](int unit_region) -> u32x4 {   // 16 bytes of region (u * RPU + r)
         return __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)woff, unit_region * 64, 0);
@@ -298,18 +351,45 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     // no branch (a branch around a load makes the compiler drain every load
     // in flight, which would hold back the weight stream).
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.x), (short)0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
+        const_cast<uint16_t*>(a.x), (short)0,
+        (int)((uint32_t)(GATHER ? a.xrows : M) * (uint32_t)K * 2u), 0x00020000);
     u32x4 xr[XPL > 0 ? XPL : 1];
-#pragma unroll
-    for (int c = 0; c < XPL; ++c) {
+    // chunk c of this lane: row m of the slice (possibly >= M: zeros), chunk q
+    auto chunk_mq = [&](int c, int& m, int& q) {
         // chunk id: lane-major within blocks so one lane owns whole blocks
         const int blk = (c / CPB) * 64 + lane, part = c % CPB;
         const int cid = blk * CPB + part;
-        const int m = cid / (KW / 8), q = cid - m * (KW / 8);
-        xr[c] = __builtin_amdgcn_raw_buffer_load_b128(
-            xrs, (int)(((uint32_t)m * (uint32_t)K + (uint32_t)(k0 + q * 8)) * 2u), 0, 0);
+        m = cid / (KW / 8);
+        q = cid - m * (KW / 8);
+    };
+    if constexpr (!GATHER) {
+#pragma unroll
+        for (int c = 0; c < XPL; ++c) {
+            int m, q;
+            chunk_mq(c, m, q);
+            xr[c] = __builtin_amdgcn_raw_buffer_load_b128(
+                xrs, (int)(((uint32_t)m * (uint32_t)K + (uint32_t)(k0 + q * 8)) * 2u), 0, 0);
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);  // x first: staging it waits for nothing else
+    // gather: the index row of each chunk's GEMM row (rows past the tile
+    // read the tile's last row; their x loads are skipped below)
+    uint32_t xir[GATHER ? (XPL > 0 ? XPL : 1) : 1];
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(GATHER ? a.perm : nullptr), (short)0,
+        (GATHER && a.perm) ? a.R * 4 : 0, 0x00020000);
+    if constexpr (GATHER) {
+        const uint32_t direct = a.perm ? 0u : 1u;
+#pragma unroll
+        for (int c = 0; c < XPL; ++c) {
+            int m, q;
+            chunk_mq(c, m, q);
+            const int rho = m0 + (m < M ? m : M - 1);
+            const uint32_t pos = (uint32_t)(row_begin + rho / a.Mx);
+            const uint32_t ir = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(pos * 4u), 0, 0);
+            xir[c] = direct ? pos : ir;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // x (gather: its index rows) first
 
     // ---- 2. scale data of the slice (contiguous in the row); after x, so
     // that staging x waits only for x (loads complete in order)
@@ -320,9 +400,9 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
         constexpr uint32_t SBYTES = F::AFF ? 2u : 1u;
         const uint32_t sbytes_all = (uint32_t)a.N * (uint32_t)gpr * SBYTES;
         const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void*>(a.scales), (short)0, (int)sbytes_all, 0x00020000);
+            const_cast<unsigned char*>(scp), (short)0, (int)sbytes_all, 0x00020000);
         const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(F::AFF ? a.biases : (const uint16_t*)a.scales), (short)0,
+            const_cast<uint16_t*>(F::AFF ? bip : (const uint16_t*)scp), (short)0,
             (int)(F::AFF ? sbytes_all : 0u), 0x00020000);
         const uint32_t soff = colv ? (ncol * (uint32_t)gpr + (uint32_t)(u_begin * F::GPU)) * SBYTES
                                    : 0x80000000u;
@@ -391,6 +471,29 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
                 wbuf[p][r] = wload((u_begin + p) * F::RPU + r);
             if constexpr (DX) load_xf(xfr[p], u_begin + p);
         }
+
+    // ---- gather: x rows through lhs, issued after the weight stream (the
+    // staging below then also waits for the weight units, which were issued
+    // first)
+    if constexpr (GATHER) {
+        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t*>(a.lhs), (short)0, a.lhs ? a.R * 4 : 0, 0x00020000);
+        const uint32_t has_lhs = a.lhs ? 1u : 0u;
+#pragma unroll
+        for (int c = 0; c < XPL; ++c) {
+            const uint32_t lb = __builtin_amdgcn_raw_buffer_load_b32(lrs, (int)(xir[c] * 4u), 0, 0);
+            xir[c] = has_lhs ? lb : xir[c];       // x batch entry of the index row
+        }
+#pragma unroll
+        for (int c = 0; c < XPL; ++c) {
+            int m, q;
+            chunk_mq(c, m, q);
+            const int rho = m0 + m;
+            const uint32_t xrow = xir[c] * (uint32_t)a.Mx + (uint32_t)(rho % a.Mx);
+            const uint32_t off = m < M ? (xrow * (uint32_t)K + (uint32_t)(k0 + q * 8)) * 2u : 0x80000000u;
+            xr[c] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)off, 0, 0);
+        }
+    }
 
     // ---- 4. x slice -> LDS (fragment order) + this slice of the zero row
 #pragma unroll
@@ -540,7 +643,13 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
                 v += red[(w * 16 + m) * 16 + col];
             }
         }
-        a.y[(size_t)m * a.N + n] = (uint16_t)f32_to_bf16_rne(v);
+        size_t yrow = (size_t)m;
+        if constexpr (GATHER) {
+            const int rho = m0 + m;
+            const int pos = row_begin + rho / a.Mx;
+            yrow = (size_t)(a.perm ? a.perm[pos] : (uint32_t)pos) * a.Mx + (size_t)(rho % a.Mx);
+        }
+        a.y[yrow * a.N + n] = (uint16_t)f32_to_bf16_rne(v);
     }
 }
 
@@ -596,10 +705,13 @@ int pick_upw(int nunits, int M, bool dx) {
     return choose_upw(nunits, M, F::U, F::RPU, dx);
 }
 
+// gather_tiles > 0: the gather form, blockIdx.y over that many row tiles
+// (an upper bound; tiles past the real count leave at once).
 template <int MODE, int BITS, int G, int UPW, bool DX>
-hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
+hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, hipStream_t st) {
     constexpr int PF = UPW < QLIN_DECODE_PF ? UPW : QLIN_DECODE_PF;
     const unsigned blocks = (unsigned)((a.N + a.cols - 1) / a.cols);
+    const dim3 grid(blocks, gather_tiles > 0 ? (unsigned)gather_tiles : 1u);
     const unsigned threads = 64u * (unsigned)ks;
     const size_t shm = (DX ? 0 : (size_t)(a.M + 1) * xrow_bytes(a.K)) + (size_t)ks * 16 * 16 * 4;
     auto run = [&](auto kern) -> hipError_t {
@@ -608,21 +720,30 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, hipStream_t st) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
             if (e != hipSuccess) return e;
         }
-        kern<<<blocks, threads, shm, st>>>(a);
+        kern<<<grid, threads, shm, st>>>(a);
         return hipGetLastError();
     };
     // group sums of x instead of the all-ones MFMA: affine, one row slot, M <= 4
     constexpr bool XSOK = Fmt<MODE, BITS, G>::AFF && Fmt<MODE, BITS, G>::S == 1 && !DX;
-    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX, XSOK>);
-    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX, XSOK>);
-    if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, XSOK>);
-    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, false>);
+    if constexpr (!DX) {
+        if (gather_tiles > 0) {   // a tile holds 1 .. a.M rows
+            if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, XSOK, true>);
+            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, true>);
+        }
+    }
+    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX, XSOK, false>);
+    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX, XSOK, false>);
+    if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, XSOK, false>);
+    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, false, false>);
 }
 
+// Plain form (perm == null) or gather form: rows bucketed by expert into
+// tiles of tile_rows GEMM rows (launch_bucket with the same tile height).
 template <int MODE, int BITS, int G, bool DX>
-hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
+hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets, int tile_rows,
+                      hipStream_t st) {
     using F = Fmt<MODE, BITS, G>;
-    DecodeArgs a;
+    DecodeArgs a{};
     a.x = (const uint16_t*)q.x;
     a.wq = q.wq;
     a.scales = q.scales;
@@ -632,17 +753,44 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     a.N = (int)q.N;
     a.K = (int)q.K;
     a.cols = decode_columns(a.N);
+    int gather_tiles = 0;
+    if (tile_rows < 0) {
+        // direct gather form: one tile per index row, its rows = x rows per index row
+        a.Mx = (int)q.M;
+        a.M = (int)q.M;
+        a.rhs = q.rhs;
+        a.lhs = q.lhs;
+        a.E = (int)q.E;
+        a.R = (int)q.R;
+        a.xrows = (int)(q.batch_x * q.M);
+        gather_tiles = (int)q.R;
+    } else if (perm) {
+        // GEMM rows = index rows x rows per index row; a tile is tile_rows of
+        // one expert, so the tile count is at most rows / tile_rows plus one
+        // per expert that has rows
+        const int64_t rows = q.R * q.M;
+        a.Mx = (int)q.M;
+        a.M = tile_rows;
+        a.perm = perm;
+        a.offsets = offsets;
+        a.tiles = offsets + (q.E + 1);
+        a.lhs = q.lhs;
+        a.E = (int)q.E;
+        a.R = (int)q.R;
+        a.xrows = (int)(q.batch_x * q.M);
+        gather_tiles = (int)(rows / tile_rows + (q.E < q.R ? q.E : q.R));
+    }
     const int mreg = a.M > 4 ? 4 : a.M;
     const int nunits = a.K / F::U;
     const int upw = pick_upw<MODE, BITS, G>(nunits, a.M, DX);
     if (upw == 0) return hipErrorNotSupported;
     const int ks = nunits / upw;
     switch (upw) {
-    case 16: return launch_upw<MODE, BITS, G, 16, DX>(a, ks, mreg, st);
-    case 8: return launch_upw<MODE, BITS, G, 8, DX>(a, ks, mreg, st);
-    case 4: return launch_upw<MODE, BITS, G, 4, DX>(a, ks, mreg, st);
-    case 2: return launch_upw<MODE, BITS, G, 2, DX>(a, ks, mreg, st);
-    default: return launch_upw<MODE, BITS, G, 1, DX>(a, ks, mreg, st);
+    case 16: return launch_upw<MODE, BITS, G, 16, DX>(a, ks, mreg, gather_tiles, st);
+    case 8: return launch_upw<MODE, BITS, G, 8, DX>(a, ks, mreg, gather_tiles, st);
+    case 4: return launch_upw<MODE, BITS, G, 4, DX>(a, ks, mreg, gather_tiles, st);
+    case 2: return launch_upw<MODE, BITS, G, 2, DX>(a, ks, mreg, gather_tiles, st);
+    default: return launch_upw<MODE, BITS, G, 1, DX>(a, ks, mreg, gather_tiles, st);
     }
 }
 
@@ -682,27 +830,28 @@ bool decode_direct_x(const QmmArgs& q) {
 }
 
 template <bool DX>
-hipError_t launch_mode(const QmmArgs& q, hipStream_t st) {
+hipError_t launch_mode(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets, int tile_rows,
+                       hipStream_t st) {
     switch (q.mode) {
-    case MXFP4: return launch_fmt<MXFP4, 4, 32, DX>(q, st);
-    case NVFP4: return launch_fmt<NVFP4, 4, 16, DX>(q, st);
-    case MXFP8: return launch_fmt<MXFP8, 8, 32, DX>(q, st);
+    case MXFP4: return launch_fmt<MXFP4, 4, 32, DX>(q, perm, offsets, tile_rows, st);
+    case NVFP4: return launch_fmt<NVFP4, 4, 16, DX>(q, perm, offsets, tile_rows, st);
+    case MXFP8: return launch_fmt<MXFP8, 8, 32, DX>(q, perm, offsets, tile_rows, st);
     default: break;
     }
     if constexpr (DX) {
         return hipErrorNotSupported;
     } else {
         if (q.bits == 4)
-            return q.group_size == 32 ? launch_fmt<AFFINE, 4, 32, false>(q, st)
-                 : q.group_size == 64 ? launch_fmt<AFFINE, 4, 64, false>(q, st)
-                                      : launch_fmt<AFFINE, 4, 128, false>(q, st);
+            return q.group_size == 32 ? launch_fmt<AFFINE, 4, 32, false>(q, perm, offsets, tile_rows, st)
+                 : q.group_size == 64 ? launch_fmt<AFFINE, 4, 64, false>(q, perm, offsets, tile_rows, st)
+                                      : launch_fmt<AFFINE, 4, 128, false>(q, perm, offsets, tile_rows, st);
         if (q.bits == 8)
-            return q.group_size == 32 ? launch_fmt<AFFINE, 8, 32, false>(q, st)
-                 : q.group_size == 64 ? launch_fmt<AFFINE, 8, 64, false>(q, st)
-                                      : launch_fmt<AFFINE, 8, 128, false>(q, st);
-        return q.group_size == 32 ? launch_fmt<AFFINE, 2, 32, false>(q, st)
-             : q.group_size == 64 ? launch_fmt<AFFINE, 2, 64, false>(q, st)
-                                  : launch_fmt<AFFINE, 2, 128, false>(q, st);
+            return q.group_size == 32 ? launch_fmt<AFFINE, 8, 32, false>(q, perm, offsets, tile_rows, st)
+                 : q.group_size == 64 ? launch_fmt<AFFINE, 8, 64, false>(q, perm, offsets, tile_rows, st)
+                                      : launch_fmt<AFFINE, 8, 128, false>(q, perm, offsets, tile_rows, st);
+        return q.group_size == 32 ? launch_fmt<AFFINE, 2, 32, false>(q, perm, offsets, tile_rows, st)
+             : q.group_size == 64 ? launch_fmt<AFFINE, 2, 64, false>(q, perm, offsets, tile_rows, st)
+                                  : launch_fmt<AFFINE, 2, 128, false>(q, perm, offsets, tile_rows, st);
     }
 }
 
@@ -728,17 +877,46 @@ bool qmm_decode_supports(const QmmArgs& q) {
 
 hipError_t launch_qmm_decode(const QmmArgs& q0, hipStream_t st) {
     if (!qmm_decode_supports(q0)) return hipErrorNotSupported;
-    if (decode_direct_x(q0)) return launch_mode<true>(q0, st);
+    if (decode_direct_x(q0)) return launch_mode<true>(q0, nullptr, nullptr, 0, st);
     const int64_t rpp = decode_rows_per_pass(q0);
     for (int64_t m0 = 0; m0 < q0.M; m0 += rpp) {
         QmmArgs q = q0;
         q.M = (q0.M - m0) < rpp ? (q0.M - m0) : rpp;
         q.x = (const uint16_t*)q0.x + m0 * q0.K;
         q.y = (uint16_t*)q0.y + m0 * q0.N;
-        hipError_t e = launch_mode<false>(q, st);
+        hipError_t e = launch_mode<false>(q, nullptr, nullptr, 0, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+int qmm_decode_gather_tile_rows(const QmmArgs& q) {
+    if (!q.transpose || q.x_dtype != QLIN_BF16 || q.R <= 0 || q.M < 1 || q.E < 1) return 0;
+    const int64_t rows = q.R * q.M;
+    int rt;
+    if (rows * 2 <= q.E && q.M <= 4) rt = -1;   // direct: rows rarely share an expert
+    else if (rows <= 2 * q.E) rt = 4;
+    else if (rows <= 8 * q.E) rt = (q.mode == AFFINE && q.bits == 2 && q.group_size == 32) ? 8 : 16;
+    else return 0;
+    if (q.N < 1 || q.K > (1 << 20) || q.K % 8 != 0) return 0;
+    // 32-bit buffer offsets into x, one expert's weight and its scales; grid y
+    if (q.batch_x * q.M * q.K * 2 >= (1LL << 31) || q.N * q.K * q.bits / 8 >= (1LL << 31)) return 0;
+    if (q.N * (q.K / q.group_size) * 2 >= (1LL << 31) || q.R * 4 >= (1LL << 31)) return 0;
+    if ((rt > 0 ? rows / rt + q.E : q.R) >= 65536) return 0;
+    // 16-byte aligned weight rows of every expert, x rows and per-wave scale blocks
+    if (((uintptr_t)q.wq & 15) != 0 || ((uintptr_t)q.x & 15) != 0) return 0;
+    if (((uintptr_t)q.scales & 15) != 0 || ((uintptr_t)q.biases & 15) != 0) return 0;
+    if ((q.N * q.K * q.bits / 8) % 16 != 0) return 0;
+    const int64_t gpr = q.K / q.group_size;
+    if ((q.mode == AFFINE ? gpr * 2 : gpr) % 16 != 0) return 0;
+    return decode_shape_ok(q, rt > 0 ? rt : q.M) ? rt : 0;
+}
+
+hipError_t launch_qmm_decode_gather(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,
+                                    int tile_rows, hipStream_t st) {
+    if (tile_rows == 0 || tile_rows != qmm_decode_gather_tile_rows(q)) return hipErrorNotSupported;
+    if (tile_rows > 0 && (!perm || !offsets)) return hipErrorInvalidValue;
+    return launch_mode<false>(q, tile_rows > 0 ? perm : nullptr, offsets, tile_rows, st);
 }
 
 }  // namespace qlin

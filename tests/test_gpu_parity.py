@@ -412,6 +412,39 @@ def test_gather_skewed_experts(path):
                     sorted_indices=True, path=path, wid=69)
 
 
+@pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8),
+                                         ("affine", 32, 4)] + MICRO_CASES)
+def test_gather_decode_kernel(mode, g, bits):
+    """Small-M kernel's gather form (forced): one tile per index row (far
+    fewer rows than experts, no bucketing), row tiles of 4 (few rows per
+    expert) and of 16 (8 for 2-bit g32), experts split over several tiles,
+    empty experts, 2 activation rows per index row, lhs given or identity,
+    indices unsorted and pre-sorted."""
+    K, N = 1024, 200
+    # decode sizes: 3 tokens x top-4 of 16 experts (tile height 4)
+    T, E, k = 3, 16, 4
+    rhs = synth.topk_distinct(T, E, k, 71)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+    run_gather_case(T, 1, K, N, E, rhs, lhs, bits=bits, g=g, mode=mode, path="decode", wid=71)
+    order = np.argsort(rhs.ravel(), kind="stable")
+    run_gather_case(T, 1, K, N, E, rhs.ravel()[order], (order // k).astype(np.uint32), bits=bits,
+                    g=g, mode=mode, sorted_indices=True, path="decode", wid=71)
+    # 2 rows per index row: expert 3 gets 3 index rows = 6 GEMM rows (2 tiles of 4)
+    run_gather_case(6, 2, K, N, 8, [3, 0, 3, 5, 3, 1], None, bits=bits, g=g, mode=mode,
+                    path="decode", wid=72)
+    # far fewer rows than experts: no bucketing, one tile per index row
+    # (expert 3 twice, 1 and 2 rows per index row, lhs given or identity)
+    run_gather_case(4, 1, K, N, 16, [3, 9, 3, 14, 0, 7], [0, 1, 2, 3, 1, 0], bits=bits, g=g,
+                    mode=mode, path="decode", wid=74)
+    run_gather_case(3, 2, K, N, 16, [5, 5, 12], None, bits=bits, g=g, mode=mode, path="decode",
+                    wid=75)
+    # tile height 16: 20 rows over 4 experts, one of them with 17 (2 tiles)
+    rhs2 = np.array([2] * 17 + [0, 3, 0], np.uint32)
+    np.random.default_rng(4).shuffle(rhs2)
+    run_gather_case(5, 1, K, N, 4, rhs2, np.arange(20, dtype=np.uint32) % 5, bits=bits, g=g,
+                    mode=mode, path="decode", wid=73)
+
+
 def test_gather_sorted_flag_is_only_a_hint():
     """Flag set on indices that are not sorted: results must not change."""
     run_gather_case(6, 1, 256, 64, 4, [3, 0, 1, 3, 2, 0], None, sorted_indices=True, wid=67)
