@@ -162,9 +162,14 @@ def main():
                 "us": sec * 1e6, "TFLOP/s": tf, "frac_mfma": tf / MFMA_PEAK_TFLOPS["bf16"],
                 "GB/s": alg / sec / 1e9, "flops": flops, "alg_bytes": alg, "steps": n}
 
-    def moe_case(sorted_indices, wid=301):
-        E, N, K, T, k = 64, 1536, 2048, 512, 8
+    def moe_case(sorted_indices, T=512, wid=301):
+        """gather_qmm over 64 stacked experts, T tokens x top-8 distinct experts;
+        cycles through >= 512 MB of weight copies like the decode cases."""
+        E, N, K, k = 64, 1536, 2048, 8
         qw = make_weight((E, N, K), wid, "affine", 64, 4, True)
+        per = qw_bytes(qw)
+        ncopy = max(1, math.ceil(ROTATE_BYTES / per))
+        copies = [qw] + [clone_qw(qw) for _ in range(ncopy - 1)]
         x, _ = synth.normal((T, 1, K), 1.0, wid, synth.ACT, "bf16")
         x = x.to(dev)
         rhs = torch.from_numpy(synth.topk_distinct(T, E, k, wid).astype("int32"))
@@ -174,21 +179,26 @@ def main():
             rhs_f, lhs_f = rhs.reshape(-1)[order], lhs.reshape(-1)[order]
         else:
             rhs_f, lhs_f = rhs.reshape(-1), lhs.reshape(-1)
+        touched = len(set(rhs_f.tolist()))
         rhs_f, lhs_f = rhs_f.to(dev), lhs_f.to(dev)
         R = rhs_f.numel()
         ws = torch.empty(qm.gather_qmm_workspace_bytes(R, E), dtype=torch.uint8, device=dev)
         y = torch.empty((R, 1, N), dtype=torch.bfloat16, device=dev)
-        fns = [lambda: qm.gather_qmm(x, qw, rhs_f, lhs_f, sorted_indices=sorted_indices,
-                                     workspace=ws, out=y)]
-        n = max(10, args.steps // 4)
+        fns = [lambda c=c: qm.gather_qmm(x, c, rhs_f, lhs_f, sorted_indices=sorted_indices,
+                                         workspace=ws, out=y) for c in copies]
+        n = max(len(fns), (max(10, args.steps // 4) // len(fns)) * len(fns))
         sec = timed(fns, n, min(args.warmup, 5))
-        alg = qw_bytes(qw) + x.numel() * 2 + y.numel() * 2 + 2 * R * 4
+        # algorithmic bytes: the experts the indices touch, each once
+        alg = per * touched // E + x.numel() * 2 + y.numel() * 2 + 2 * R * 4
         flops = 2 * R * N * K
+        del copies, fns
+        torch.cuda.empty_cache()
         return {"workload": f"MoE gather_qmm affine 4-bit g64 E{E} N{N} K{K} tokens{T} top{k} "
                             f"sorted={'true' if sorted_indices else 'false'}",
                 "us": sec * 1e6, "GB/s": alg / sec / 1e9, "frac_hbm": alg / sec / 1e9 / HBM_PEAK_GBS,
                 "TFLOP/s": flops / sec / 1e12,
-                "frac_mfma": flops / sec / 1e12 / MFMA_PEAK_TFLOPS["bf16"], "steps": n}
+                "frac_mfma": flops / sec / 1e12 / MFMA_PEAK_TFLOPS["bf16"], "alg_bytes": alg,
+                "experts_touched": touched, "copies": ncopy, "steps": n}
 
     results = []
     log("decode headline: affine int4 g64 M1 N14336 K4096")
@@ -225,6 +235,10 @@ def main():
     if args.only == "all":
         for s in (False, True):
             r = moe_case(s)
+            results.append(r)
+            log(json.dumps(r))
+        for T in (1, 8):   # decode-sized expert batches
+            r = moe_case(False, T=T, wid=305)
             results.append(r)
             log(json.dumps(r))
     if args.copy_probe:
