@@ -137,9 +137,10 @@ bool qmm_decode_supports(const QmmArgs& a);
 int qmm_decode_gather_tile_rows(const QmmArgs& a);
 hipError_t launch_qmm_decode_gather(const QmmArgs& a, const uint32_t* row_perm,
                                     const uint32_t* expert_offsets, int tile_rows, hipStream_t s);
-// MoE bucketing: counts rows per expert, scans, and writes the stable
-// permutation of rows sorted by expert (skipped when rows are pre-sorted).
-// rows_per_tile sets the row-tile prefix written after the offsets.
+// MoE bucketing: counts rows per expert, scans, and writes a permutation of
+// the rows grouped by expert (any order within an expert; skipped when the
+// rows are pre-sorted). rows_per_tile sets the row-tile prefix written after
+// the offsets.
 hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, int sorted,
                          int rows_per_tile, void* workspace, uint32_t** row_perm,
                          uint32_t** expert_offsets, hipStream_t s);
