@@ -780,6 +780,12 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
         a.xrows = (int)(q.batch_x * q.M);
         gather_tiles = (int)(rows / tile_rows + (q.E < q.R ? q.E : q.R));
     }
+#ifndef QLIN_GATHER_COLS16
+#define QLIN_GATHER_COLS16 1
+#endif
+    // the gather grid spans many row tiles (several rounds of workgroups):
+    // full 16-column blocks halve the workgroups and their fixed costs
+    if (gather_tiles > 0 && QLIN_GATHER_COLS16) a.cols = 16;
     const int mreg = a.M > 4 ? 4 : a.M;
     const int nunits = a.K / F::U;
     const int upw = pick_upw<MODE, BITS, G>(nunits, a.M, DX);
