@@ -329,37 +329,60 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
 }
 
 // One workgroup: per-expert counts, exclusive scan into offsets and row-tile
-// prefix, then rows scattered into expert order (or the identity when the
-// caller's indices are verified non-decreasing).
-__global__ void __launch_bounds__(1024) bucket_kernel(const uint32_t* __restrict__ rhs, int R,
-                                                      int E, int M, int BMrows, int sorted,
-                                                      uint32_t* __restrict__ offsets,
-                                                      uint32_t* __restrict__ tiles,
-                                                      uint32_t* __restrict__ perm) {
+// prefix, then rows placed into expert order (or the identity when the
+// caller's indices are verified non-decreasing). Four waves; each thread
+// keeps the experts of its first BCACHE rows in registers, so rhs is read
+// once (the kernel is latency-bound: a few barriers and memory round trips).
+constexpr int BUCKET_THREADS = 256;
+constexpr int BCACHE = 16;
+
+__global__ void __launch_bounds__(BUCKET_THREADS) bucket_kernel(const uint32_t* __restrict__ rhs, int R,
+                                                                int E, int M, int BMrows, int sorted,
+                                                                uint32_t* __restrict__ offsets,
+                                                                uint32_t* __restrict__ tiles,
+                                                                uint32_t* __restrict__ perm) {
+    constexpr int NT = BUCKET_THREADS;
     extern __shared__ uint32_t sh[];
     uint32_t* cnt = sh;          // [E]
     uint32_t* cur = sh + E;      // [E]
     __shared__ int unsorted;
     __shared__ uint32_t carry[2];
-    const int tid = threadIdx.x, nt = blockDim.x;
+    __shared__ uint32_t wsum[NT / 64][2];
+    const int tid = threadIdx.x;
     if (tid == 0) {
         unsorted = 0;
         carry[0] = carry[1] = 0;
     }
-    for (int e = tid; e < E; e += nt) cnt[e] = 0;
-    __syncthreads();
-    for (int r = tid; r < R; r += nt) {
-        atomicAdd(&cnt[rhs[r]], 1u);
-        if (sorted && r + 1 < R && rhs[r] > rhs[r + 1]) unsorted = 1;
+    for (int e = tid; e < E; e += NT) cnt[e] = 0;
+    // rows tid + c * NT, c < BCACHE: experts kept in registers
+    uint32_t rv[BCACHE];
+#pragma unroll
+    for (int c = 0; c < BCACHE; ++c) {
+        const int r = tid + c * NT;
+        rv[c] = r < R ? rhs[r] : 0u;
     }
     __syncthreads();
-    // exclusive scans of counts and of row tiles, in chunks of nt experts
-    for (int base = 0; base < E; base += nt) {
+#pragma unroll
+    for (int c = 0; c < BCACHE; ++c) {
+        const int r = tid + c * NT;
+        if (r < R) {
+            atomicAdd(&cnt[rv[c]], 1u);
+            if (sorted && r + 1 < R && rv[c] > rhs[r + 1]) unsorted = 1;
+        }
+    }
+    for (int r = tid + BCACHE * NT; r < R; r += NT) {
+        const uint32_t v = rhs[r];
+        atomicAdd(&cnt[v], 1u);
+        if (sorted && r + 1 < R && v > rhs[r + 1]) unsorted = 1;
+    }
+    __syncthreads();
+    // exclusive scans of counts and of row tiles, in chunks of NT experts
+    for (int base = 0; base < E; base += NT) {
         const int e = base + tid;
         const uint32_t c = e < E ? cnt[e] : 0u;
         const uint32_t t = (uint32_t)(((uint64_t)c * M + BMrows - 1) / BMrows);
         uint32_t vc = c, vt = t;
-        // inclusive warp scans, then across warps through shared memory
+        // inclusive wave scans, then across waves through shared memory
         for (int off = 1; off < 64; off <<= 1) {
             uint32_t uc = __shfl_up(vc, off, 64), ut = __shfl_up(vt, off, 64);
             if ((tid & 63) >= off) {
@@ -367,7 +390,6 @@ __global__ void __launch_bounds__(1024) bucket_kernel(const uint32_t* __restrict
                 vt += ut;
             }
         }
-        __shared__ uint32_t wsum[16][2];
         if ((tid & 63) == 63) {
             wsum[tid >> 6][0] = vc;
             wsum[tid >> 6][1] = vt;
@@ -384,7 +406,7 @@ __global__ void __launch_bounds__(1024) bucket_kernel(const uint32_t* __restrict
             cur[e] = pc + vc - c;
         }
         __syncthreads();
-        if (tid == nt - 1) {
+        if (tid == NT - 1) {
             carry[0] = pc + vc;
             carry[1] = pt + vt;
         }
@@ -394,14 +416,15 @@ __global__ void __launch_bounds__(1024) bucket_kernel(const uint32_t* __restrict
         offsets[E] = carry[0];
         tiles[E] = carry[1];
     }
-    __syncthreads();
     if (sorted && !unsorted) {
-        for (int r = tid; r < R; r += nt) perm[r] = (uint32_t)r;
+        for (int r = tid; r < R; r += NT) perm[r] = (uint32_t)r;
     } else {
-        for (int r = tid; r < R; r += nt) {
-            const uint32_t pos = atomicAdd(&cur[rhs[r]], 1u);
-            perm[pos] = (uint32_t)r;
+#pragma unroll
+        for (int c = 0; c < BCACHE; ++c) {
+            const int r = tid + c * NT;
+            if (r < R) perm[atomicAdd(&cur[rv[c]], 1u)] = (uint32_t)r;
         }
+        for (int r = tid + BCACHE * NT; r < R; r += NT) perm[atomicAdd(&cur[rhs[r]], 1u)] = (uint32_t)r;
     }
 }
 
@@ -475,8 +498,8 @@ hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, i
     const size_t shm = (size_t)2 * E * sizeof(uint32_t);
     if (shm > 64 * 1024) return hipErrorInvalidValue;
     if (rows_per_tile < 1) return hipErrorInvalidValue;
-    bucket_kernel<<<1, 1024, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted, *offsets,
-                                        *offsets + (E + 1), *perm);
+    bucket_kernel<<<1, BUCKET_THREADS, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted,
+                                                  *offsets, *offsets + (E + 1), *perm);
     return hipGetLastError();
 }
 
