@@ -264,9 +264,14 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 // and its y rows go back to the index rows' places. The index loads are
 // issued first, the weight stream next, and the x loads (which need them)
 // last, so the weight stream never waits on the index chain.
-template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER>
-__global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
+// CB = 2 (direct x fragments, microscaled codes): a wave covers two column
+// blocks with the same x fragments, halving the x the workgroups re-read
+// from L2 (at M = 16 those reads, not the weight stream, set the time);
+// at most 8 waves per workgroup then, for the registers.
+template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER, int CB>
+__global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
+    static_assert(CB == 1 || (CB == 2 && DX && !F::AFF && !GATHER), "two column blocks: direct-x path");
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
     static_assert(!GATHER || !DX, "the gather form stages x in LDS");
@@ -321,19 +326,26 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
 
     const int k0 = wv * KW;                       // first k of this wave
     const int u_begin = wv * UPW;
-    const int n0 = blockIdx.x * a.cols;
+    const int n0 = blockIdx.x * a.cols * CB;
     const int wpr = K / F::PER;                   // words per weight row
     const int gpr = K / G;                        // groups per weight row
     // Lane row i carries output column n0 + i. Columns past this workgroup's
     // share (or past N) read zeros through the buffer range check: no memory
     // traffic, never stored.
-    const bool colv = i < a.cols && n0 + i < a.N;
-    const uint32_t ncol = (uint32_t)(n0 + i);
+    bool colv[CB];
+    uint32_t ncol[CB], woff[CB];
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+        ncol[b] = (uint32_t)(n0 + b * a.cols + i);
+        colv[b] = i < a.cols && (int)ncol[b] < a.N;
+    }
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(wqp), (short)0, (int)((uint32_t)a.N * (uint32_t)wpr * 4u), 0x00020000);
-    const uint32_t woff = colv ? (ncol * (uint32_t)wpr + 4u * j) * 4u : 0x80000000u;
-    auto wload = [&](int unit_region) -> u32x4 {   // 16 bytes of region (u * RPU + r)
-        return __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)woff, unit_region * 64, 0);
+#pragma unroll
+    for (int b = 0; b < CB; ++b)
+        woff[b] = colv[b] ? (ncol[b] * (uint32_t)wpr + 4u * j) * 4u : 0x80000000u;
+    auto wload = [&](int b, int unit_region) -> u32x4 {   // 16 bytes of region (u * RPU + r)
+        return __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)woff[b], unit_region * 64, 0);
     };
 
     // ---- 1. this wave's x slice (staged path): M rows x KW elements, in blocks of BE
@@ -395,8 +407,9 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     // that staging x waits only for x (loads complete in order)
     constexpr int SB = F::AFF ? UPW * F::GPU * 2 : UPW * F::GPU;  // bytes per slice
     constexpr int SW = (SB + 3) / 4;
-    uint32_t sraw[SW], zraw[F::AFF ? SW : 1];
-    {
+    uint32_t sraw[CB][SW], zraw[F::AFF ? SW : 1];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
         constexpr uint32_t SBYTES = F::AFF ? 2u : 1u;
         const uint32_t sbytes_all = (uint32_t)a.N * (uint32_t)gpr * SBYTES;
         const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -404,13 +417,14 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
         const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(F::AFF ? bip : (const uint16_t*)scp), (short)0,
             (int)(F::AFF ? sbytes_all : 0u), 0x00020000);
-        const uint32_t soff = colv ? (ncol * (uint32_t)gpr + (uint32_t)(u_begin * F::GPU)) * SBYTES
-                                   : 0x80000000u;
+        const uint32_t soff = colv[cb] ? (ncol[cb] * (uint32_t)gpr + (uint32_t)(u_begin * F::GPU)) * SBYTES
+                                       : 0x80000000u;
         if constexpr (SB >= 16) {
 #pragma unroll
             for (int v = 0; v < SB / 16; ++v) {
                 const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)soff, 16 * v, 0);
-                sraw[4 * v] = t[0]; sraw[4 * v + 1] = t[1]; sraw[4 * v + 2] = t[2]; sraw[4 * v + 3] = t[3];
+                sraw[cb][4 * v] = t[0]; sraw[cb][4 * v + 1] = t[1];
+                sraw[cb][4 * v + 2] = t[2]; sraw[cb][4 * v + 3] = t[3];
                 if constexpr (F::AFF) {
                     const u32x4 tz = __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)soff, 16 * v, 0);
                     zraw[4 * v] = tz[0]; zraw[4 * v + 1] = tz[1]; zraw[4 * v + 2] = tz[2]; zraw[4 * v + 3] = tz[3];
@@ -418,16 +432,16 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
             }
         } else if constexpr (SB == 8) {
             const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(srs, (int)soff, 0, 0);
-            sraw[0] = t[0]; sraw[1] = t[1];
+            sraw[cb][0] = t[0]; sraw[cb][1] = t[1];
             if constexpr (F::AFF) {
                 const u32x2 tz = __builtin_amdgcn_raw_buffer_load_b64(zrs, (int)soff, 0, 0);
                 zraw[0] = tz[0]; zraw[1] = tz[1];
             }
         } else if constexpr (SB == 4) {
-            sraw[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)soff, 0, 0);
+            sraw[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)soff, 0, 0);
             if constexpr (F::AFF) zraw[0] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)soff, 0, 0);
         } else {
-            sraw[0] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)soff, 0, 0);
+            sraw[cb][0] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)soff, 0, 0);
             if constexpr (F::AFF) zraw[0] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)soff, 0, 0);
         }
     }
@@ -462,13 +476,15 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     };
 
     // ---- 3. the first PF weight units (and their x fragments)
-    u32x4 wbuf[PF][F::RPU];
+    u32x4 wbuf[PF][CB][F::RPU];
 #pragma unroll
     for (int p = 0; p < PF; ++p)
         if (p < UPW) {
 #pragma unroll
-            for (int r = 0; r < F::RPU; ++r)
-                wbuf[p][r] = wload((u_begin + p) * F::RPU + r);
+            for (int b = 0; b < CB; ++b)
+#pragma unroll
+                for (int r = 0; r < F::RPU; ++r)
+                    wbuf[p][b][r] = wload(b, (u_begin + p) * F::RPU + r);
             if constexpr (DX) load_xf(xfr[p], u_begin + p);
         }
 
@@ -550,22 +566,28 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
 
     const unsigned char* abase = smem + arow * rowb + j * 16;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dsum = {0.f, 0.f, 0.f, 0.f};
-    float ysum[MREG];
+    f32x4 acc[CB], dsum = {0.f, 0.f, 0.f, 0.f};
+    float ysum[CB][MREG];
 #pragma unroll
-    for (int r = 0; r < MREG; ++r) ysum[r] = 0.f;
+    for (int b = 0; b < CB; ++b) {
+        acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < MREG; ++r) ysum[b][r] = 0.f;
+    }
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int uu = 0; uu < UPW; ++uu) {
         const int u = u_begin + uu;
-        u32x4 wcur[F::RPU];
+        u32x4 wcur[CB][F::RPU];
 #pragma unroll
-        for (int r = 0; r < F::RPU; ++r) {
-            wcur[r] = wbuf[uu % PF][r];
-            xpose4(wcur[r]);
-        }
+        for (int b = 0; b < CB; ++b)
+#pragma unroll
+            for (int r = 0; r < F::RPU; ++r) {
+                wcur[b][r] = wbuf[uu % PF][b][r];
+                xpose4(wcur[b][r]);
+            }
         u32x4 xcur[XF];
         if constexpr (DX) {
 #pragma unroll
@@ -574,8 +596,10 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
         // refill the ring slot with unit uu + PF
         if (uu + PF < UPW) {
 #pragma unroll
-            for (int r = 0; r < F::RPU; ++r)
-                wbuf[uu % PF][r] = wload((u + PF) * F::RPU + r);
+            for (int b = 0; b < CB; ++b)
+#pragma unroll
+                for (int r = 0; r < F::RPU; ++r)
+                    wbuf[uu % PF][b][r] = wload(b, (u + PF) * F::RPU + r);
             if constexpr (DX) load_xf(xfr[uu % PF], u + PF);
         }
 #pragma unroll
@@ -589,23 +613,26 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
                 else av = *(const u32x4*)(abase + gs * 64);
                 const bool first = F::AFF && (ls % F::WS == 0);
                 if constexpr (F::AFF && !XS) dsum = mfma_bf16(av, ones, first ? zero4 : dsum);
-                float sc = 0.f;
-                if constexpr (!F::AFF) {
-                    int byte;
-                    if constexpr (MODE == NVFP4) byte = uu * F::GPU + 2 * ls + (j >> 1);
-                    else byte = uu * F::GPU + ls;
-                    const int wd = (MODE == NVFP4) ? (uu * F::GPU + 2 * ls) / 4 : byte / 4;
-                    sc = scale_byte_to_f32<MODE>((sraw[wd] >> (8 * (byte & 3))) & 0xFFu);
+#pragma unroll
+                for (int b = 0; b < CB; ++b) {
+                    float sc = 0.f;
+                    if constexpr (!F::AFF) {
+                        int byte;
+                        if constexpr (MODE == NVFP4) byte = uu * F::GPU + 2 * ls + (j >> 1);
+                        else byte = uu * F::GPU + ls;
+                        const int wd = (MODE == NVFP4) ? (uu * F::GPU + 2 * ls) / 4 : byte / 4;
+                        sc = scale_byte_to_f32<MODE>((sraw[b][wd] >> (8 * (byte & 3))) & 0xFFu);
+                    }
+                    const u32x4 bv = unpack<MODE, BITS, G>(wcur[b][r], t, sc);
+                    acc[b] = mfma_bf16(av, bv, first ? zero4 : acc[b]);
                 }
-                const u32x4 bv = unpack<MODE, BITS, G>(wcur[r], t, sc);
-                acc = mfma_bf16(av, bv, first ? zero4 : acc);
                 if constexpr (F::AFF) {
                     if (ls % F::WS == F::WS - 1) {
                         // window done: apply the group's scale and bias
                         const int wi = ls / F::WS;
                         const int gw = uu * F::GPU + (F::S == 2 ? 2 * wi : wi);
                         const int sh = (F::S == 2) ? 16 * (j >> 1) : 16 * (gw & 1);
-                        const float s = bf16_bits_to_f32((sraw[gw >> 1] >> sh) & 0xFFFFu);
+                        const float s = bf16_bits_to_f32((sraw[0][gw >> 1] >> sh) & 0xFFFFu);
                         const float z = bf16_bits_to_f32((zraw[gw >> 1] >> sh) & 0xFFFFu);
                         const float zz = __builtin_fmaf(-F::OFF, s, z);
 #pragma unroll
@@ -613,8 +640,8 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
                             float xs;
                             if constexpr (XS) xs = xgroup_sum(rr, gw);
                             else xs = dsum[rr];
-                            ysum[rr] = __builtin_fmaf(s, acc[rr], ysum[rr]);
-                            ysum[rr] = __builtin_fmaf(zz, xs, ysum[rr]);
+                            ysum[0][rr] = __builtin_fmaf(s, acc[0][rr], ysum[0][rr]);
+                            ysum[0][rr] = __builtin_fmaf(zz, xs, ysum[0][rr]);
                         }
                     }
                 }
@@ -623,24 +650,29 @@ __global__ void __launch_bounds__(1024) qmm_decode_kernel(DecodeArgs a) {
     }
     if constexpr (!F::AFF) {
 #pragma unroll
-        for (int rr = 0; rr < MREG; ++rr) ysum[rr] = acc[rr];
+        for (int b = 0; b < CB; ++b)
+#pragma unroll
+            for (int rr = 0; rr < MREG; ++rr) ysum[b][rr] = acc[b][rr];
     }
 
-    // ---- cross-wave reduction: red[wave][row][col]
+    // ---- cross-wave reduction: red[wave][block][row][col]
 #pragma unroll
-    for (int rr = 0; rr < MREG; ++rr) red[(wv * 16 + 4 * j + rr) * 16 + i] = ysum[rr];
+    for (int b = 0; b < CB; ++b)
+#pragma unroll
+        for (int rr = 0; rr < MREG; ++rr) red[((wv * CB + b) * 16 + 4 * j + rr) * 16 + i] = ysum[b][rr];
     __syncthreads();
-    for (int o = tid; o < M * 16; o += 64 * KS) {
-        const int m = o >> 4, col = o & 15;
-        const int n = n0 + col;
+    for (int o = tid; o < CB * M * 16; o += 64 * KS) {
+        const int b = o / (M * 16), mo = o - b * (M * 16);
+        const int m = mo >> 4, col = mo & 15;
+        const int n = n0 + b * a.cols + col;
         if (n >= a.N || col >= a.cols) continue;
         float v = 0.f;
         for (int w = 0; w < KS; ++w) {
             if constexpr (F::S == 2) {
-                v += red[(w * 16 + m) * 16 + col];
-                v += red[(w * 16 + 8 + m) * 16 + col];
+                v += red[((w * CB + b) * 16 + m) * 16 + col];
+                v += red[((w * CB + b) * 16 + 8 + m) * 16 + col];
             } else {
-                v += red[(w * 16 + m) * 16 + col];
+                v += red[((w * CB + b) * 16 + m) * 16 + col];
             }
         }
         size_t yrow = (size_t)m;
@@ -707,13 +739,14 @@ int pick_upw(int nunits, int M, bool dx) {
 
 // gather_tiles > 0: the gather form, blockIdx.y over that many row tiles
 // (an upper bound; tiles past the real count leave at once).
-template <int MODE, int BITS, int G, int UPW, bool DX>
+template <int MODE, int BITS, int G, int UPW, bool DX, int CB = 1>
 hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, hipStream_t st) {
     constexpr int PF = UPW < QLIN_DECODE_PF ? UPW : QLIN_DECODE_PF;
-    const unsigned blocks = (unsigned)((a.N + a.cols - 1) / a.cols);
+    if (CB == 2 && ks > 8) return hipErrorNotSupported;   // 512-thread kernels
+    const unsigned blocks = (unsigned)((a.N + a.cols * CB - 1) / (a.cols * CB));
     const dim3 grid(blocks, gather_tiles > 0 ? (unsigned)gather_tiles : 1u);
     const unsigned threads = 64u * (unsigned)ks;
-    const size_t shm = (DX ? 0 : (size_t)(a.M + 1) * xrow_bytes(a.K)) + (size_t)ks * 16 * 16 * 4;
+    const size_t shm = (DX ? 0 : (size_t)(a.M + 1) * xrow_bytes(a.K)) + (size_t)ks * CB * 16 * 16 * 4;
     auto run = [&](auto kern) -> hipError_t {
         if (shm > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -725,16 +758,22 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, h
     };
     // group sums of x instead of the all-ones MFMA: affine, one row slot, M <= 4
     constexpr bool XSOK = Fmt<MODE, BITS, G>::AFF && Fmt<MODE, BITS, G>::S == 1 && !DX;
-    if constexpr (!DX) {
-        if (gather_tiles > 0) {   // a tile holds 1 .. a.M rows
-            if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, XSOK, true>);
-            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, true>);
+    if constexpr (CB == 2) {
+        // direct x, microscaled: rows past 4 in registers (MREG 4)
+        return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, true, false, false, 2>);
+    } else {
+        if constexpr (!DX) {
+            if (gather_tiles > 0) {   // a tile holds 1 .. a.M rows
+                if (XSOK && a.M <= 4)
+                    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, XSOK, true, 1>);
+                return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, true, 1>);
+            }
         }
+        if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX, XSOK, false, 1>);
+        if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX, XSOK, false, 1>);
+        if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, XSOK, false, 1>);
+        return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, false, false, 1>);
     }
-    if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, DX, XSOK, false>);
-    if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, DX, XSOK, false>);
-    if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, XSOK, false>);
-    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, DX, false, false>);
 }
 
 // Plain form (perm == null) or gather form: rows bucketed by expert into
@@ -791,6 +830,26 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     const int upw = pick_upw<MODE, BITS, G>(nunits, a.M, DX);
     if (upw == 0) return hipErrorNotSupported;
     const int ks = nunits / upw;
+#ifndef QLIN_DECODE_DX_CB
+#define QLIN_DECODE_DX_CB 2
+#endif
+    if constexpr (DX && QLIN_DECODE_DX_CB == 2) {
+        // two column blocks per wave (at most 8 waves: longer slices)
+        int upw2 = upw;
+        while (upw2 < 16 && nunits / upw2 > 8) upw2 <<= 1;
+        if (nunits % upw2 == 0 && nunits / upw2 <= 8) {
+            DecodeArgs a2 = a;
+            a2.cols = decode_columns((a.N + 1) / 2);
+            const int ks2 = nunits / upw2;
+            switch (upw2) {
+            case 16: return launch_upw<MODE, BITS, G, 16, true, 2>(a2, ks2, mreg, 0, st);
+            case 8: return launch_upw<MODE, BITS, G, 8, true, 2>(a2, ks2, mreg, 0, st);
+            case 4: return launch_upw<MODE, BITS, G, 4, true, 2>(a2, ks2, mreg, 0, st);
+            case 2: return launch_upw<MODE, BITS, G, 2, true, 2>(a2, ks2, mreg, 0, st);
+            default: return launch_upw<MODE, BITS, G, 1, true, 2>(a2, ks2, mreg, 0, st);
+            }
+        }
+    }
     switch (upw) {
     case 16: return launch_upw<MODE, BITS, G, 16, DX>(a, ks, mreg, gather_tiles, st);
     case 8: return launch_upw<MODE, BITS, G, 8, DX>(a, ks, mreg, gather_tiles, st);
