@@ -202,3 +202,32 @@ def test_moe_gather_full_size(moe_inputs, sorted_indices):
     err = sample_err(got, want)
     print(f"moe full sorted={sorted_indices}: sampled err {err:.3e}", flush=True)
     assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_moe_decode_sizes_full_size(moe_inputs, T):
+    """Decode-sized expert batches on the full 64 x [1536, 2048] int4 stack, in
+    the launch configuration the benchmark times (automatic path: one tile
+    per index row at 1 token, 4-row expert tiles at 8 tokens)."""
+    qw, wb, _, _, _ = moe_inputs
+    E, K, k = 64, 2048, 8
+    x, xb = synth.normal((T, 1, K), 1.0, 305, synth.ACT, "bf16")
+    rhs = synth.topk_distinct(T, E, k, 305)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+    rhs_f, lhs_f = rhs.reshape(-1), lhs.reshape(-1)
+    y = qm.gather_qmm(x.to(DEV), qw, torch.from_numpy(rhs_f.astype(np.int32)).to(DEV),
+                      torch.from_numpy(lhs_f.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (T * k, 1, 1536)
+    cols = pick(1536, 48, 43 + T)
+    yg = gpu_np(y[:, 0, :])
+    got, want = [], []
+    for r in range(T * k):
+        e, t = int(rhs_f[r]), int(lhs_f[r])
+        ref = oracle.quantize(np.ascontiguousarray(wb[e][cols]), "bf16", 64, 4)
+        y_ref = oracle.quantized_matmul(np.ascontiguousarray(xb[t]), "bf16", *ref, True, 64, 4)
+        got.append(yg[r, cols])
+        want.append(y_ref[0])
+    err = sample_err(np.stack(got), np.stack(want))
+    print(f"moe decode T{T}: sampled err {err:.3e}", flush=True)
+    assert err <= TOL_BF16
