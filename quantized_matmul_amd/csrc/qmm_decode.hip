@@ -662,7 +662,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
         for (int rr = 0; rr < MREG; ++rr) red[((wv * CB + b) * 16 + 4 * j + rr) * 16 + i] = ysum[b][rr];
     __syncthreads();
     for (int o = tid; o < CB * M * 16; o += 64 * KS) {
-        const int b = o / (M * 16), mo = o - b * (M * 16);
+        const int b = CB == 1 ? 0 : o / (M * 16), mo = o - b * (M * 16);
         const int m = mo >> 4, col = mo & 15;
         const int n = n0 + b * a.cols + col;
         if (n >= a.N || col >= a.cols) continue;
