@@ -17,6 +17,7 @@ Functions and what they follow (page titles and sections):
   quantized_matmul    "EMLX.Quantization" quantized_matmul;
                       "Emily.Quantization.Layers" quantized_dense (layouts);
                       mlx-rs ``quantized_matmul`` and test_quantized_matmul.
+  quantized_dense     "Emily.Quantization.Layers" quantized_dense (the bias).
   gather_qmm          "EMLX.Quantization" gather_quantized_matmul; mlx-rs
                       ``gather_qmm`` and test_gather_qmm.
 Readings of points the pages leave open are stated in ``qlin_oracle.c``.
@@ -62,10 +63,12 @@ def _load():
     lib.oracle_dequantize.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, cs, vp, i32]
     lib.oracle_quantized_matmul.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i64, i32, i32,
                                             i32, cs, vp]
+    lib.oracle_quantized_dense.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i64, i32, i32,
+                                           i32, cs, vp, i32, ctypes.c_double, vp]
     lib.oracle_gather_qmm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp, vp,
                                       i64, i32, i32, i32, cs, vp]
     for f in ("oracle_quantize", "oracle_dequantize", "oracle_quantized_matmul",
-              "oracle_gather_qmm"):
+              "oracle_quantized_dense", "oracle_gather_qmm"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -162,6 +165,38 @@ def quantized_matmul(x, x_dtype, wq, scales, biases, transpose=True, group_size=
         _ptr(None if biases is None else np.ascontiguousarray(biases)), DTYPES[sd], N,
         int(bool(transpose)), group_size, bits, mode.encode(), _ptr(y))
     _check(rc, "quantized_matmul")
+    return y
+
+
+def quantized_dense(x, x_dtype, wq, scales, biases, bias=None, bias_dtype="f32", bias_value=0.0,
+                    transpose=True, group_size=64, bits=4, mode="affine", scale_dtype=None):
+    """y (float64) = quantized_matmul(...) + bias.
+
+    bias: N values (one per output column; bf16/f16 as uint16 bits, f32 as
+    float32), or None, and then the number bias_value (taken in fp32) is
+    added to every output.
+    """
+    x = np.ascontiguousarray(x)
+    wq = np.ascontiguousarray(wq)
+    if transpose:
+        N, K = wq.shape[0], wq.shape[1] * 32 // bits
+    else:
+        K, N = wq.shape[0], wq.shape[1] * 32 // bits
+    M = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    if x.shape[-1] != K:
+        raise OracleError("x's last dim does not match W")
+    if bias is not None:
+        bias = np.ascontiguousarray(bias)
+        if bias.size != N:
+            raise OracleError("a tensor bias holds one value per output column")
+    y = np.zeros(x.shape[:-1] + (N,), np.float64)
+    sd = scale_dtype or ("u8" if mode != "affine" else x_dtype)
+    rc = _load().oracle_quantized_dense(
+        _ptr(x), DTYPES[x_dtype], M, x.shape[-1], _ptr(wq), _ptr(np.ascontiguousarray(scales)),
+        _ptr(None if biases is None else np.ascontiguousarray(biases)), DTYPES[sd], N,
+        int(bool(transpose)), group_size, bits, mode.encode(), _ptr(bias), DTYPES[bias_dtype],
+        float(bias_value), _ptr(y))
+    _check(rc, "quantized_dense")
     return y
 
 

@@ -493,6 +493,30 @@ int oracle_quantized_matmul(const void* x, int x_dtype, int64_t M, int64_t K, co
     return OR_OK;
 }
 
+/* quantized_dense ([LAY] quantized_dense: x times the quantized W, plus a
+ * bias that is a tensor or a number, 0 when omitted): the quantized_matmul
+ * above, then the bias added to every output.
+ * READING: a tensor bias holds one value per output column (N values, the
+ * dense layer's bias) and is broadcast over the rows of y; a number is taken
+ * in fp32 (rounded to nearest even), the precision of the accumulation it
+ * joins. y stays fp64, before any rounding to the output dtype. */
+int oracle_quantized_dense(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* wq,
+                           const void* scales, const void* biases, int scale_dtype, int64_t N,
+                           int transpose, int group_size, int bits, const char* mode_str,
+                           const void* bias, int bias_dtype, double bias_value, double* y) {
+    if (bias && dtype_fmt(bias_dtype) < 0) return OR_EINVAL;
+    if (!bias && !isfinite(bias_value)) return OR_EINVAL;
+    int rc = oracle_quantized_matmul(x, x_dtype, M, K, wq, scales, biases, scale_dtype, N,
+                                     transpose, group_size, bits, mode_str, y);
+    if (rc != OR_OK) return rc;
+    double number = round_store(bias_value, FMT_F32);
+    if (!bias && !isfinite(number)) return OR_EINVAL;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] += bias ? load_val(bias, bias_dtype, n) : number;
+    return OR_OK;
+}
+
 /* gather_qmm ([EMLX] gather_quantized_matmul; [RS] gather_qmm doc and
  * test_gather_qmm): x [B, M, K], W stacked [E, N, K] (transpose) or
  * [E, K, N]; for each r, y[r] = x[lhs[r]] . dequant(W[rhs[r]])^T, with

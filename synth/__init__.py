@@ -4,12 +4,13 @@ This module holds no quantization or matmul arithmetic: it only draws random
 numbers and rounds them to the storage dtype a workload asks for (by torch's
 own dtype conversion). Every draw is numpy PCG64 seeded with
 ``[workload_id, tensor_id]`` (tensor 0 = weight, 1 = activation,
-2 = indices), so the oracle and the GPU path see identical bytes.
+2 = indices, 3 = the dense layer's bias), so the oracle and the GPU path see
+identical bytes.
 """
 import numpy as np
 import torch
 
-WEIGHT, ACT, INDEX = 0, 1, 2
+WEIGHT, ACT, INDEX, BIAS = 0, 1, 2, 3
 
 
 def rng(workload_id: int, tensor_id: int) -> np.random.Generator:

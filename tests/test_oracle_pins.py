@@ -376,6 +376,82 @@ def test_rs_quantized_matmul_transpose_false():
     assert np.abs(y - y_hat).max() < 1e-3
 
 
+# ------------------------------------------------------- quantized_dense
+# "Emily.Quantization.Layers" quantized_dense: x times the quantized W plus
+# a bias (a tensor or a number, 0 by default).
+
+def _bias_bits(vals, dtype):
+    v = np.asarray(vals, np.float32)
+    if dtype == "f32":
+        return v
+    t = torch.from_numpy(v).to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    assert np.array_equal(t.float().numpy(), v)      # the values are exact in dtype
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("transpose", [True, False])
+@pytest.mark.parametrize("bdtype", ["f32", "bf16", "f16"])
+def test_dense_grid_exact_equals_integer_matmul_plus_bias(transpose, bdtype):
+    """Exact weights and integer x: y equals x.W^T (or x.W) plus the column
+    bias broadcast over the rows, exactly in fp64 (a bias indexed by row, or
+    by the wrong layout's axis, fails: M != N and every column differs)."""
+    N, K, M = 128, 256, 5
+    rows, cols = (N, K) if transpose else (K, N)
+    w, q, s, z = _grid_exact(rows, cols, 64, 4, seed=77)
+    x = np.random.default_rng(5).integers(-3, 4, size=(M, K)).astype(np.float32)
+    b = (np.arange(N) - 40) / 4.0                       # k/4: exact in f32, bf16 and f16
+    wq, sc, bi = oracle.quantize(w, "f32", 64, 4)
+    y = oracle.quantized_dense(x, "f32", wq, sc, bi, _bias_bits(b, bdtype), bdtype,
+                               transpose=transpose, group_size=64, bits=4)
+    W = w.astype(np.float64)
+    ref = x.astype(np.float64) @ (W.T if transpose else W) + b[None, :]
+    assert y.shape == (M, N)
+    assert np.array_equal(y, ref)
+
+
+def test_dense_number_bias_is_taken_in_fp32():
+    N, K, M = 32, 128, 3
+    w, q, s, z = _grid_exact(N, K, 32, 4, seed=78)
+    x = np.random.default_rng(6).integers(-3, 4, size=(M, K)).astype(np.float32)
+    wq, sc, bi = oracle.quantize(w, "f32", 32, 4)
+    base = x.astype(np.float64) @ w.astype(np.float64).T   # exact small integers
+    y = oracle.quantized_dense(x, "f32", wq, sc, bi, None, bias_value=0.1, group_size=32, bits=4)
+    d = y - base                                           # exact: base is a small integer
+    assert np.all(d == float(np.float32(0.1))) and float(np.float32(0.1)) != 0.1
+
+
+def test_dense_zero_bias_is_quantized_matmul():
+    tw, wb = synth.normal((48, 128), 0.02, 79, 0, "bf16")
+    tx, xb = synth.normal((4, 128), 1.0, 79, 1, "bf16")
+    wq, sc, bi = oracle.quantize(wb, "bf16", 64, 4)
+    y0 = oracle.quantized_matmul(xb, "bf16", wq, sc, bi, True, 64, 4)
+    assert np.array_equal(oracle.quantized_dense(xb, "bf16", wq, sc, bi), y0)
+    zeros = _bias_bits(np.zeros(48), "bf16")
+    assert np.array_equal(oracle.quantized_dense(xb, "bf16", wq, sc, bi, zeros, "bf16"), y0)
+
+
+def test_dense_zero_input_gives_the_bias():
+    """x = 0: every row of y is the bias vector (the broadcast is over rows)."""
+    tw, wb = synth.normal((40, 64), 0.02, 80, 0, "bf16")
+    wq, sc, bi = oracle.quantize(wb, "bf16", 32, 4)
+    tb, bb = synth.normal((40,), 1.0, 80, synth.BIAS, "bf16")
+    x = np.zeros((7, 64), np.uint16)                   # bf16 +0
+    y = oracle.quantized_dense(x, "bf16", wq, sc, bi, bb, "bf16", group_size=32, bits=4)
+    assert np.array_equal(y, np.broadcast_to(bf16_to_f32(bb).astype(np.float64), (7, 40)))
+
+
+def test_dense_rejects_bad_bias():
+    tw, wb = synth.normal((40, 64), 0.02, 81, 0, "bf16")
+    wq, sc, bi = oracle.quantize(wb, "bf16", 32, 4)
+    x = np.zeros((2, 64), np.uint16)
+    with pytest.raises(oracle.OracleError):
+        oracle.quantized_dense(x, "bf16", wq, sc, bi, np.zeros(39, np.float32), group_size=32, bits=4)
+    with pytest.raises(oracle.OracleError):
+        oracle.quantized_dense(x, "bf16", wq, sc, bi, None, bias_value=float("inf"), group_size=32, bits=4)
+    with pytest.raises(oracle.OracleError):      # finite in fp64, not in fp32
+        oracle.quantized_dense(x, "bf16", wq, sc, bi, None, bias_value=1e39, group_size=32, bits=4)
+
+
 def test_page_example_shapes():
     # "Emily.QuantizedWeight" from_dense / to_dense examples
     t, w = synth.iota((4, 64))
