@@ -125,6 +125,31 @@ qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, 
                                   void* stream);
 
 /*
+ * qlin_quantized_dense -- the dense layer on a quantized weight: y = x . W^T
+ * (or x . W) plus a bias, fused into the matmul's output stage
+ * ("Emily.Quantization.Layers" quantized_dense: x @ W (+ bias), the bias a
+ * tensor or a number, 0 by default).
+ *   x, wq, scales, biases, transpose, group_size, bits, mode, y: as for
+ *       qlin_quantized_matmul.
+ *   bias        device pointer to N values of bias_dtype (QLIN_F32, QLIN_F16
+ *               or QLIN_BF16), one per output column, added to every row;
+ *               or NULL, and then the number bias_value is added to every
+ *               output (0 gives qlin_quantized_matmul's result).
+ * The bias is added in fp32 to the fp32 accumulation of each output before
+ * its one rounding into y's dtype. bias must be 4-byte aligned for QLIN_F32
+ * and 2-byte aligned otherwise. Errors as for qlin_quantized_matmul, plus
+ * QLIN_ERR_INVALID_ARGUMENT for a bias dtype outside those three or a
+ * bias_value that is not finite once rounded to fp32 (the number is taken
+ * in fp32).
+ */
+qlin_status qlin_quantized_dense(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                 const uint32_t* wq, const void* scales, const void* biases,
+                                 qlin_dtype scale_dtype, int64_t N, int transpose,
+                                 int group_size, int bits, const char* mode, const void* bias,
+                                 qlin_dtype bias_dtype, double bias_value, void* y,
+                                 void* stream);
+
+/*
  * qlin_gather_qmm_workspace_bytes -- device workspace qlin_gather_qmm needs
  * for R index rows over E experts (bucket offsets, counts and the row
  * permutation). Always > 0.

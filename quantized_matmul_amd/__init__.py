@@ -7,8 +7,8 @@ computation runs in the library's kernels. There is no CPU fallback: if the
 library is not built, every call raises.
 
 Raw ABI calls (same names as the C functions, minus the ``qlin_`` prefix):
-``quantize``, ``dequantize``, ``quantized_matmul``, ``gather_qmm`` operate on
-explicit tensors. ``QuantizedWeight`` bundles the packed weight with its
+``quantize``, ``dequantize``, ``quantized_matmul``, ``quantized_dense``,
+``gather_qmm`` operate on explicit tensors. ``QuantizedWeight`` bundles the packed weight with its
 metadata, mirroring the field set of the "Emily.QuantizedWeight" page
 (value, scales, biases, group_size, bits, transpose, mode).
 """
@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     quantize,
+    quantized_dense,
     quantized_matmul,
     MODE_DEFAULTS,
 )

@@ -50,12 +50,15 @@ def load_library():
     lib.qlin_dequantize.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, cs, vp, i32, vp]
     lib.qlin_quantized_matmul.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i64, i32, i32, i32,
                                           cs, vp, vp]
+    lib.qlin_quantized_dense.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i64, i32, i32, i32,
+                                         cs, vp, i32, ctypes.c_double, vp, vp]
     lib.qlin_gather_qmm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp, vp,
                                     i64, i32, i32, i32, cs, i32, vp, sz, vp, vp]
     lib.qlin_gather_qmm_workspace_bytes.argtypes = [i64, i64]
     lib.qlin_gather_qmm_workspace_bytes.restype = sz
     lib.qlin_last_error.restype = ctypes.c_char_p
-    for f in ("qlin_quantize", "qlin_dequantize", "qlin_quantized_matmul", "qlin_gather_qmm"):
+    for f in ("qlin_quantize", "qlin_dequantize", "qlin_quantized_matmul", "qlin_quantized_dense",
+              "qlin_gather_qmm"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -179,6 +182,48 @@ def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
                                    _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype], N,
                                    int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),
                                    _ptr(y), _stream(dev))
+    _check(rc)
+    return y
+
+
+def quantized_dense(x: torch.Tensor, qw: QuantizedWeight, bias=0,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qlin_quantized_dense: x @ W (+ bias) ("Emily.Quantization.Layers",
+    quantized_dense). bias is a number, or a float tensor of N values (one
+    per output column) on x's device; it is added in fp32 before the output's
+    one rounding.
+    """
+    lib = load_library()
+    dev = _dev(x)
+    _dev(qw.value)
+    if qw.value.dim() != 2:
+        raise ValueError("quantized_dense takes a 2-D quantized weight")
+    per = 32 // qw.bits
+    if qw.transpose:
+        N, K = qw.value.shape[0], qw.value.shape[1] * per
+    else:
+        K, N = qw.value.shape[0], qw.value.shape[1] * per
+    if x.shape[-1] != K:
+        raise ValueError(f"x's last dim {x.shape[-1]} does not match the weight's K={K}")
+    bias_t, bias_value, bias_dt = None, 0.0, _DTYPE[torch.float32]
+    if isinstance(bias, torch.Tensor):
+        _dev(bias)
+        if bias.device != dev:
+            raise ValueError("bias must be on x's device")
+        if bias.numel() != N or bias.dim() < 1 or bias.shape[-1] != N:
+            raise ValueError(f"a tensor bias holds one value per output column ({N})")
+        if bias.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+            raise ValueError("bias must be float32, bfloat16 or float16")
+        bias_t = bias.contiguous()
+        bias_dt = _DTYPE[bias_t.dtype]
+    else:
+        bias_value = float(bias)
+    M = x.numel() // K if K else 0
+    y = _out(out, tuple(x.shape[:-1]) + (N,), x.dtype, dev)
+    rc = lib.qlin_quantized_dense(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value),
+                                  _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype], N,
+                                  int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),
+                                  _ptr(bias_t), bias_dt, bias_value, _ptr(y), _stream(dev))
     _check(rc)
     return y
 

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -158,10 +159,16 @@ qlin_status qlin_dequantize(const uint32_t* wq, const void* scales, const void* 
                          "dequantize");
 }
 
-qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
-                                  const uint32_t* wq, const void* scales, const void* biases,
-                                  qlin_dtype scale_dtype, int64_t N, int transpose, int group_size,
-                                  int bits, const char* mode, void* y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by quantized_matmul and quantized_dense: checks, then the kernel
+// that takes the shape, with the dense layer's bias in its output stage.
+qlin_status qmm_entry(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, const uint32_t* wq,
+                      const void* scales, const void* biases, qlin_dtype scale_dtype, int64_t N,
+                      int transpose, int group_size, int bits, const char* mode,
+                      const qlin::OutBias& ob, void* y, void* stream) {
     int m;
     if (N <= 0 || K <= 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "N and K must be positive");
     qlin_status st = check_mode(mode, group_size, bits, transpose ? K : N, &m);
@@ -191,7 +198,44 @@ qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, 
     a.group_size = group_size;
     a.bits = bits;
     a.mode = m;
+    a.ob = ob;
     return run_qmm(a, nullptr, nullptr, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                  const uint32_t* wq, const void* scales, const void* biases,
+                                  qlin_dtype scale_dtype, int64_t N, int transpose, int group_size,
+                                  int bits, const char* mode, void* y, void* stream) {
+    const qlin::OutBias none{nullptr, 0.f, qlin::OB_NONE, QLIN_F32};
+    return qmm_entry(x, x_dtype, M, K, wq, scales, biases, scale_dtype, N, transpose, group_size,
+                     bits, mode, none, y, stream);
+}
+
+qlin_status qlin_quantized_dense(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                 const uint32_t* wq, const void* scales, const void* biases,
+                                 qlin_dtype scale_dtype, int64_t N, int transpose, int group_size,
+                                 int bits, const char* mode, const void* bias, qlin_dtype bias_dtype,
+                                 double bias_value, void* y, void* stream) {
+    qlin::OutBias ob{nullptr, 0.f, qlin::OB_NONE, QLIN_F32};
+    if (bias) {
+        if (!is_float_dtype(bias_dtype))
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "bias must be f32, f16 or bf16");
+        const uintptr_t align = bias_dtype == QLIN_F32 ? 4 : 2;
+        if ((uintptr_t)bias % align)
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "bias is not aligned to its element size");
+        ob = {bias, 0.f, qlin::OB_COLUMN, (int)bias_dtype};
+    } else {
+        // the number is taken in fp32, like the accumulation it is added to
+        if (!std::isfinite((float)bias_value))
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "bias value must be finite in fp32");
+        if (bias_value != 0.0) ob = {nullptr, (float)bias_value, qlin::OB_SCALAR, QLIN_F32};
+    }
+    return qmm_entry(x, x_dtype, M, K, wq, scales, biases, scale_dtype, N, transpose, group_size,
+                     bits, mode, ob, y, stream);
 }
 
 size_t qlin_gather_qmm_workspace_bytes(int64_t R, int64_t E) {

@@ -48,6 +48,30 @@ __device__ __forceinline__ void store_f(void* p, int64_t i, float v) {
     else ((uint16_t*)p)[i] = (uint16_t)f32_to_f16_rne(v);
 }
 
+// Bias of the dense layer ("Emily.Quantization.Layers", quantized_dense: the
+// layer adds a bias, a tensor or a number, to x times W): none, one number for
+// every output, or one value per output column (a vector of N elements).
+// Added in fp32 to the accumulated output before its single rounding.
+enum OutBiasKind : int { OB_NONE = 0, OB_SCALAR = 1, OB_COLUMN = 2 };
+struct OutBias {
+    const void* p;   // [N] (OB_COLUMN), dtype below
+    float value;     // OB_SCALAR
+    int kind;
+    int dtype;       // QLIN_F32, QLIN_BF16 or QLIN_F16
+};
+
+__device__ __forceinline__ float out_bias_at(const OutBias& b, int64_t n) {
+    if (b.kind != OB_COLUMN) return b.value;
+    if (b.dtype == QLIN_F32) return ((const float*)b.p)[n];
+    const uint32_t h = ((const uint16_t*)b.p)[n];
+    return b.dtype == QLIN_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+// v plus the bias of output column n (v unchanged without a bias).
+__device__ __forceinline__ float add_out_bias(const OutBias& b, int64_t n, float v) {
+    return b.kind == OB_NONE ? v : v + out_bias_at(b, n);
+}
+
 // ------------------------------------------------- small formats (decoding)
 
 // E8M0 scale byte: 2^(b-127). b = 0 is the fp32 subnormal 2^-127.
@@ -98,6 +122,7 @@ struct QmmArgs {
     int64_t E;
     const uint32_t* lhs;         // [R] or null
     const uint32_t* rhs;         // [R] or null
+    OutBias ob;                  // dense-layer bias (plain matmul only)
 };
 
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int g,

@@ -190,6 +190,7 @@ struct DecodeArgs {
     const uint32_t* rhs;      // [R] expert of each index row (direct form)
     const uint32_t* lhs;      // [R] x batch entry of each index row, or null (identity)
     int E, Mx, R, xrows;      // experts; x rows per index row; index rows; rows of x
+    OutBias ob;               // dense-layer bias (plain form)
 };
 
 // LDS layout: (M+1) rows of K/8 16-byte chunks (row M is zero), each row
@@ -681,7 +682,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
             const int pos = row_begin + rho / a.Mx;
             yrow = (size_t)(a.perm ? a.perm[pos] : (uint32_t)pos) * a.Mx + (size_t)(rho % a.Mx);
         }
-        a.y[yrow * a.N + n] = (uint16_t)f32_to_bf16_rne(v);
+        a.y[yrow * a.N + n] = (uint16_t)f32_to_bf16_rne(add_out_bias(a.ob, n, v));
     }
 }
 
@@ -788,6 +789,7 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     a.scales = q.scales;
     a.biases = (const uint16_t*)q.biases;
     a.y = (uint16_t*)q.y;
+    a.ob = q.ob;
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;

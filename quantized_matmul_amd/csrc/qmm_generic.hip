@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(256) qmm_generic_t_kernel(QmmArgs a, int64_t t
     }
     if (lane == 0) {
         for (int i = 0; i < ROWS_PER_WAVE; ++i)
-            if (rho0 + i < total_rows) store_f<XDT>(a.y, (rho0 + i) * a.N + n, acc[i]);
+            if (rho0 + i < total_rows) store_f<XDT>(a.y, (rho0 + i) * a.N + n, add_out_bias(a.ob, n, acc[i]));
     }
 }
 
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(256) qmm_generic_n_kernel(QmmArgs a, int64_t t
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             float v = red[0][lane][e] + red[1][lane][e] + red[2][lane][e] + red[3][lane][e];
-            store_f<XDT>(a.y, rho * a.N + c * PER + e, v);
+            store_f<XDT>(a.y, rho * a.N + c * PER + e, add_out_bias(a.ob, c * PER + e, v));
         }
     }
 }

@@ -32,6 +32,7 @@ struct NtArgs {
     const uint16_t* biases;
     uint16_t* y;         // bf16 [M, N]
     int M, N, K;
+    OutBias ob;          // dense-layer bias
 };
 
 // Lane (rr, cl) = (lane / WPB, lane % WPB) handles packed word c0 + cl of
@@ -213,7 +214,8 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
             float v = 0.f;
 #pragma unroll 4
             for (int w = 0; w < NWAVES; ++w) v += red[(w * WPB + l) * PER + e];
-            if (cc < wcols) a.y[(size_t)m * N + cc * PER + e] = (uint16_t)f32_to_bf16_rne(v);
+            if (cc < wcols)
+                a.y[(size_t)m * N + cc * PER + e] = (uint16_t)f32_to_bf16_rne(add_out_bias(a.ob, cc * PER + e, v));
         }
         __syncthreads();
     }
@@ -248,6 +250,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     a.scales = q.scales;
     a.biases = (const uint16_t*)q.biases;
     a.y = (uint16_t*)q.y;
+    a.ob = q.ob;
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;

@@ -51,6 +51,7 @@ struct PrefillArgs {
     const uint32_t* tiles;    // [E+1] row-tile prefix of each expert
     int E, B;
     int xgm;                  // plain form: the 8 XCDs as an xgm x (8/xgm) grid of tile blocks (0: rows)
+    OutBias ob;               // dense-layer bias (plain form)
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -185,7 +186,7 @@ __device__ __forceinline__ void dequant_chunk(const Chunk<WORDS>& c, float s, fl
 
 // BM activation rows x BN weight rows per workgroup of WM x WN waves; CPC
 // codes per dequant chunk (8 or 16), chunks dealt round-robin to threads.
-template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC, bool GATHER, int WPF>
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC, bool GATHER, int WPF, bool OB>
 __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a) {
     constexpr int NTH = WM * WN * 64;
     constexpr int PER = 32 / BITS;
@@ -401,11 +402,30 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         }
     };
 
+    // accumulators start at zero, or (OB: the dense layer's bias, a separate
+    // instantiation so the plain kernel's code is untouched) at the bias of
+    // the lane's output columns n = n0 + wn_*NW + 16t + 4j + r, added once
+    // per output; the output stage is the plain matmul's
     f32x4 acc[NT][MT];
+    if constexpr (!OB) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int s = 0; s < MT; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < MT; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f32x4 b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = n0 + wn_ * NW + t * 16 + 4 * j + r;
+                b[r] = n < a.N ? out_bias_at(a.ob, n) : 0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < MT; ++s) acc[t][s] = b;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bias loads before the tile loads
+    }
 
     const int nk = a.K / BK;
     // WPF register sets hold the packed codes of steps kt+1 .. kt+WPF; set
@@ -544,7 +564,8 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
 #endif
 
 
-template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, bool GATHER>
+template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, bool GATHER,
+          bool OB = false>
 hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     // a chunk holds at least one packed dword
     constexpr int CPC = CPC0 < 32 / BITS ? 32 / BITS : CPC0;
@@ -568,9 +589,9 @@ hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     };
     // the code prefetch depth must divide the number of 64-wide steps
     const int nk = t.K / BK;
-    if (nk % WPF == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, WPF>);
-    if (nk % 2 == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 2>);
-    return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 1>);
+    if (nk % WPF == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, WPF, OB>);
+    if (nk % 2 == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 2, OB>);
+    return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 1, OB>);
 }
 
 // XCD grid for the plain form: the 8 XCDs take an xgm x (8/xgm) grid of
@@ -601,6 +622,7 @@ hipError_t launch_plain(const PrefillArgs& t0, hipStream_t st) {
     const double w_bytes = (double)t.N * t.K * BITS / 8.0, x_bytes = (double)t.M * t.K * 2.0;
     t.xgm = xcd_grid_rows(ntm, ntn, w_bytes, x_bytes);
     const int grid = (int)(ntm * ntn);
+    if (t.ob.kind != OB_NONE) return launch_cfg<MODE, BITS, G, BM, BN, WM, WN, CPC0, false, true>(t, grid, st);
     return launch_cfg<MODE, BITS, G, BM, BN, WM, WN, CPC0, false>(t, grid, st);
 }
 
@@ -637,6 +659,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     t.M = (int)q.M;
     t.N = (int)q.N;
     t.K = (int)q.K;
+    t.ob = q.ob;
     int cfg = pick_cfg(q.M, q.N);
     if (const char* e = getenv("QLIN_PREFILL_TILE")) cfg = atoi(e) % 4;  // tests of each shape
     switch (cfg) {

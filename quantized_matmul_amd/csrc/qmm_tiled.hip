@@ -59,6 +59,7 @@ struct TiledArgs {
     const uint32_t* offsets; // [E+1] index-row offsets per expert
     const uint32_t* tiles;   // [E+1] row-tile prefix per expert
     int E;
+    OutBias ob;              // dense-layer bias (plain form)
 };
 
 // Dequantize one 16-byte chunk of packed codes (128/BITS codes starting at
@@ -271,11 +272,29 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
         }
     };
 
+    // accumulators start at zero, or at the dense-layer bias of the lane's
+    // output columns n = n0 + wn*NW + 16t + 4j + r (added once per output;
+    // the output stage is the plain matmul's)
     f32x4 acc[NT][MT];
+    if (a.ob.kind == OB_NONE) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int s = 0; s < MT; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < MT; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f32x4 b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = n0 + wn * NW + t * 16 + 4 * j + r;
+                b[r] = n < a.N ? out_bias_at(a.ob, n) : 0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < MT; ++s) acc[t][s] = b;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // bias loads before the tile loads
 
     const int nk = a.K / BK;
     gload(0);
@@ -457,6 +476,7 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     t.M = (int)q.M;
     t.N = (int)q.N;
     t.K = (int)q.K;
+    t.ob = q.ob;
     if (q.R == 0) {
         constexpr int BM = 256, BN = 128;
         const int grid = (int)(((q.M + BM - 1) / BM) * ((q.N + BN - 1) / BN));

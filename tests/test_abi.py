@@ -31,7 +31,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"qlin_quantize", "qlin_dequantize", "qlin_quantized_matmul",
-                          "qlin_gather_qmm", "qlin_gather_qmm_workspace_bytes", "qlin_last_error"}
+                          "qlin_quantized_dense", "qlin_gather_qmm",
+                          "qlin_gather_qmm_workspace_bytes", "qlin_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -93,6 +94,29 @@ def test_quantized_matmul_rejects(lib):
     assert q(None, BF16, 1, 128, FAKE, FAKE, FAKE, BF16, 64, 1, 64, 4, b"affine", FAKE, None) == INVALID
     # M == 0 is an empty product: no-op, no device call
     assert q(None, BF16, 0, 128, None, None, FAKE, BF16, 64, 1, 64, 4, b"affine", None, None) == 0
+
+
+def test_quantized_dense_rejects(lib):
+    d = lib.qlin_quantized_dense
+    base = dict(x=FAKE, xdt=BF16, M=1, K=128, wq=FAKE, s=FAKE, b=FAKE, sdt=BF16, N=64, t=1, g=64,
+                bits=4, mode=b"affine", bias=None, bdt=F32, bval=0.0, y=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return d(*a.values())
+
+    assert call(bias=FAKE, bdt=U8) == INVALID             # bias dtype: f32, f16 or bf16
+    assert "bias" in err(lib)
+    assert call(bias=ctypes.c_void_p(0x1002), bdt=F32) == INVALID   # not 4-byte aligned
+    assert call(bias=ctypes.c_void_p(0x1001), bdt=BF16) == INVALID  # not 2-byte aligned
+    assert call(bval=float("inf")) == INVALID
+    assert call(bval=float("nan")) == INVALID
+    assert call(bval=1e39) == INVALID                     # finite in fp64, not in fp32
+    # the matmul's own checks still apply
+    assert call(K=100) == INVALID
+    assert call(xdt=F32) == INVALID
+    # M == 0: no-op, no device call (the bias is checked first)
+    assert call(x=None, M=0, wq=None, s=None, y=None, bias=FAKE, bdt=BF16) == 0
 
 
 def test_gather_rejects(lib):

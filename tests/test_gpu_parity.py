@@ -448,3 +448,65 @@ def test_gather_decode_kernel(mode, g, bits):
 def test_gather_sorted_flag_is_only_a_hint():
     """Flag set on indices that are not sorted: results must not change."""
     run_gather_case(6, 1, 256, 64, 4, [3, 0, 1, 3, 2, 0], None, sorted_indices=True, wid=67)
+
+
+# ---------------------------------------------------------------- quantized_dense
+# "Emily.Quantization.Layers" quantized_dense: x @ W plus a bias (a tensor of
+# one value per output column, or a number), fused into each kernel's output
+# stage. Oracle: the fp64 matmul plus the bias, compared at the matmul bar.
+
+DENSE_CASES = [
+    # M, N, K, bits, g, mode, x dtype, transpose, forced path
+    (1, 512, 1024, 4, 64, "affine", "bf16", True, "decode"),      # decode kernel
+    (3, 500, 1024, 4, 64, "affine", "bf16", True, "decode"),      # x group sums, ragged N
+    (9, 256, 4096, 8, 128, "affine", "bf16", True, "decode"),     # rows in two passes
+    (16, 512, 8192, 4, 32, "mxfp4", "bf16", True, "decode"),      # direct x fragments
+    (4, 1024, 512, 4, 64, "affine", "bf16", False, "decode"),     # [in, out] kernel
+    (300, 400, 512, 4, 64, "affine", "bf16", True, "prefill"),    # many-row kernel, ragged
+    (130, 256, 512, 8, 32, "mxfp8", "bf16", True, "prefill"),
+    (300, 200, 512, 4, 64, "affine", "bf16", True, "tiled"),      # LDS-tiled kernel
+    (5, 128, 256, 4, 64, "affine", "f32", True, "generic"),       # fp32 VALU kernels
+    (5, 128, 256, 4, 64, "affine", "f16", False, "generic"),
+]
+
+
+@pytest.mark.parametrize("bias_kind", ["bf16", "f32", "f16", "number"])
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: f"M{c[0]}N{c[1]}K{c[2]}{c[5]}b{c[3]}t{int(c[7])}{c[8]}")
+def test_quantized_dense(case, bias_kind):
+    M, N, K, bits, g, mode, xdtype, transpose, path = case
+    wdt = xdtype if mode == "affine" else "bf16"
+    w, wb = gpu_weight((N, K) if transpose else (K, N), 0.02, 41, wdt)
+    xt, xb = synth.normal((M, K), 1.0, 41, synth.ACT, xdtype)
+    qw, (wq, sc, bi) = quantize_both(w, wb, wdt, g, bits, mode, transpose)
+    if bias_kind == "number":
+        bias, bias_bits, bval = -0.75, None, -0.75
+    else:
+        bt, bias_bits = synth.normal((N,), 1.0, 41, synth.BIAS, bias_kind)
+        bias, bval = bt.to(DEV), 0.0
+    os.environ["QLIN_FORCE_PATH"] = path
+    y = qm.quantized_dense(xt.to(DEV), qw, bias)
+    torch.cuda.synchronize()
+    os.environ.pop("QLIN_FORCE_PATH", None)
+    yref = oracle.quantized_dense(xb, xdtype, wq, sc, bi, bias_bits,
+                                  bias_kind if bias_kind != "number" else "f32", bval,
+                                  transpose, g, bits, mode,
+                                  scale_dtype=(wdt if mode == "affine" else "u8"))
+    assert y.shape == (M, N) and y.dtype == TDT[xdtype]
+    err = normwise_rel_err(y, yref)
+    tol = tolerance(TDT[xdtype], K)
+    print(f"dense {case} bias={bias_kind}: err {err:.3e} tol {tol:.1e}", flush=True)
+    assert err <= tol
+    # the bias is really applied: without it the error is far above the bar
+    y0 = oracle.quantized_matmul(xb, xdtype, wq, sc, bi, transpose, g, bits, mode,
+                                 scale_dtype=(wdt if mode == "affine" else "u8"))
+    assert normwise_rel_err(y, y0) > 2 * tol
+
+
+def test_quantized_dense_zero_bias_is_quantized_matmul():
+    """A number bias of 0 is the plain matmul: same kernel, same bits."""
+    w, wb = gpu_weight((512, 1024), 0.02, 42, "bf16")
+    xt, _ = synth.normal((2, 1024), 1.0, 42, synth.ACT, "bf16")
+    qw = qm.quantize(w, 64, 4, "affine")
+    x = xt.to(DEV)
+    assert torch.equal(qm.quantized_dense(x, qw, 0).view(torch.int16),
+                       qm.quantized_matmul(x, qw).view(torch.int16))
