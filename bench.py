@@ -124,7 +124,12 @@ def main():
         return ms / 1e3 / steps
 
     # ------------------------------------------------------------ decode
-    def decode_case(M, N, K, bits, g, mode="affine", transpose=True, wid=101, steps=None):
+    def bias_vector(N, wid):
+        b, _ = synth.normal((N,), 1.0, wid, synth.BIAS, "bf16")
+        return b.to(dev)
+
+    def decode_case(M, N, K, bits, g, mode="affine", transpose=True, wid=101, steps=None,
+                    dense_bias=False):
         shape = (N, K) if transpose else (K, N)
         qw = make_weight(shape, wid, mode, g, bits, transpose)
         per = qw_bytes(qw)
@@ -133,32 +138,42 @@ def main():
         x, _ = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
         x = x.to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        fns = [lambda c=c: qm.quantized_matmul(x, c, out=y) for c in copies]
+        if dense_bias:   # quantized_dense: x @ W + bias (bf16, one per column)
+            b = bias_vector(N, wid)
+            fns = [lambda c=c: qm.quantized_dense(x, c, b, out=y) for c in copies]
+        else:
+            fns = [lambda c=c: qm.quantized_matmul(x, c, out=y) for c in copies]
         n = steps or args.steps
         n = max(len(fns), (n // len(fns)) * len(fns))
         sec = timed(fns, n, args.warmup)
-        alg = per + x.numel() * 2 + y.numel() * 2
+        alg = per + x.numel() * 2 + y.numel() * 2 + (N * 2 if dense_bias else 0)
         gbs = alg / sec / 1e9
         del copies, fns
         torch.cuda.empty_cache()
-        return {"workload": f"decode qmm {mode} {bits}-bit g{g} M{M} N{N} K{K} "
+        op = "quantized_dense (bf16 bias)" if dense_bias else "qmm"
+        return {"workload": f"decode {op} {mode} {bits}-bit g{g} M{M} N{N} K{K} "
                             f"transpose={'true' if transpose else 'false'}",
                 "us": sec * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
                 "TFLOP/s": 2 * M * N * K / sec / 1e12, "alg_bytes": alg, "copies": ncopy,
                 "steps": n}
 
-    def prefill_case(M, N, K, bits, g, mode="affine", wid=201, steps=None):
+    def prefill_case(M, N, K, bits, g, mode="affine", wid=201, steps=None, dense_bias=False):
         qw = make_weight((N, K), wid, mode, g, bits, True)
         x, _ = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
         x = x.to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        fns = [lambda: qm.quantized_matmul(x, qw, out=y)]
+        if dense_bias:
+            b = bias_vector(N, wid)
+            fns = [lambda: qm.quantized_dense(x, qw, b, out=y)]
+        else:
+            fns = [lambda: qm.quantized_matmul(x, qw, out=y)]
         n = steps or max(10, args.steps // 8)
         sec = timed(fns, n, min(args.warmup, 5))
         flops = 2 * M * N * K
         tf = flops / sec / 1e12
-        alg = qw_bytes(qw) + x.numel() * 2 + y.numel() * 2
-        return {"workload": f"prefill qmm {mode} {bits}-bit g{g} M{M} N{N} K{K} transpose=true",
+        alg = qw_bytes(qw) + x.numel() * 2 + y.numel() * 2 + (N * 2 if dense_bias else 0)
+        op = "quantized_dense (bf16 bias)" if dense_bias else "qmm"
+        return {"workload": f"prefill {op} {mode} {bits}-bit g{g} M{M} N{N} K{K} transpose=true",
                 "us": sec * 1e6, "TFLOP/s": tf, "frac_mfma": tf / MFMA_PEAK_TFLOPS["bf16"],
                 "GB/s": alg / sec / 1e9, "flops": flops, "alg_bytes": alg, "steps": n}
 
@@ -224,6 +239,10 @@ def main():
                                 steps=max(32, args.steps // 4))
                 results.append(r)
                 log(json.dumps(r))
+        r = decode_case(1, 14336, 4096, 4, 64, wid=101, steps=max(32, args.steps // 4),
+                        dense_bias=True)
+        results.append(r)
+        log(json.dumps(r))
     if args.only in ("all", "prefill"):
         r = prefill_case(2048, 12288, 4096, 4, 128, wid=202)
         results.append(r)
@@ -232,6 +251,9 @@ def main():
             r = prefill_case(512, 8192, 8192, bits, g, mode=mode, wid=203)
             results.append(r)
             log(json.dumps(r))
+        r = prefill_case(2048, 12288, 4096, 4, 64, wid=201, dense_bias=True)
+        results.append(r)
+        log(json.dumps(r))
     if args.only == "all":
         for s in (False, True):
             r = moe_case(s)
