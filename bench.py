@@ -177,6 +177,60 @@ def main():
                 "us": sec * 1e6, "TFLOP/s": tf, "frac_mfma": tf / MFMA_PEAK_TFLOPS["bf16"],
                 "GB/s": alg / sec / 1e9, "flops": flops, "alg_bytes": alg, "steps": n}
 
+    def quant_case(N, K, bits, g, mode="affine", wid=401):
+        """qlin_quantize of a bf16 W [N, K], then qlin_dequantize back to bf16,
+        each timed on its own, cycling input copies past the Infinity Cache;
+        algorithmic bytes: what each must read and write once."""
+        import ctypes
+        lib = qm.load_library()
+        per = 32 // bits
+        w, _ = synth.normal((N, K), 0.02, wid, synth.WEIGHT, "bf16")
+        w = w.to(dev)
+        ncopy = max(1, math.ceil(ROTATE_BYTES / (w.numel() * 2)))
+        ws = [w] + [w.clone() for _ in range(ncopy - 1)]
+        G = K // g
+        sdt = torch.bfloat16 if mode == "affine" else torch.uint8
+        outs = [(torch.empty((N, K // per), dtype=torch.int32, device=dev),
+                 torch.empty((N, G), dtype=sdt, device=dev),
+                 torch.empty((N, G), dtype=sdt, device=dev) if mode == "affine" else None)
+                for _ in range(ncopy)]
+        vp = ctypes.c_void_p
+        BF16 = 2
+
+        def stream():   # the current stream at call time (graph capture has its own)
+            return vp(torch.cuda.current_stream().cuda_stream)
+
+        def q(i):
+            wq, sc, bi = outs[i]
+            rc = lib.qlin_quantize(vp(ws[i].data_ptr()), BF16, N, K, g, bits, mode.encode(),
+                                   vp(wq.data_ptr()), vp(sc.data_ptr()),
+                                   vp(bi.data_ptr()) if bi is not None else None, stream())
+            assert rc == 0, rc
+
+        dense = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(ncopy)]
+
+        def dq(i):
+            wq, sc, bi = outs[i]
+            rc = lib.qlin_dequantize(vp(wq.data_ptr()), vp(sc.data_ptr()),
+                                     vp(bi.data_ptr()) if bi is not None else None,
+                                     BF16 if mode == "affine" else 3, N, K, g, bits,
+                                     mode.encode(), vp(dense[i].data_ptr()), BF16, stream())
+            assert rc == 0, rc
+
+        n = max(ncopy, (max(16, args.steps // 8) // ncopy) * ncopy)
+        tq = timed([lambda i=i: q(i) for i in range(ncopy)], n, min(args.warmup, 4))
+        td = timed([lambda i=i: dq(i) for i in range(ncopy)], n, min(args.warmup, 4))
+        packed = N * K * bits // 8 + N * G * (4 if mode == "affine" else 1)
+        bq = N * K * 2 + packed
+        res = []
+        for name, t, b in (("quantize", tq, bq), ("dequantize", td, bq)):
+            res.append({"workload": f"{name} {mode} {bits}-bit g{g} W bf16 [{N},{K}]",
+                        "us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
+                        "alg_bytes": b, "copies": ncopy, "steps": n})
+        del ws, outs, dense
+        torch.cuda.empty_cache()
+        return res
+
     def moe_case(sorted_indices, T=512, wid=301):
         """gather_qmm over 64 stacked experts, T tokens x top-8 distinct experts;
         cycles through >= 512 MB of weight copies like the decode cases."""
@@ -255,6 +309,10 @@ def main():
         results.append(r)
         log(json.dumps(r))
     if args.only == "all":
+        for (N, K, bits, g, mode) in [(14336, 4096, 4, 64, "affine"), (8192, 8192, 4, 32, "mxfp4")]:
+            for r in quant_case(N, K, bits, g, mode):
+                results.append(r)
+                log(json.dumps(r))
         for s in (False, True):
             r = moe_case(s)
             results.append(r)

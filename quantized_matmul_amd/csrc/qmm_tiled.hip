@@ -352,8 +352,11 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
 // caller's indices are verified non-decreasing). Four waves; each thread
 // keeps the experts of its first BCACHE rows in registers, so rhs is read
 // once (the kernel is latency-bound: a few barriers and memory round trips).
-constexpr int BUCKET_THREADS = 256;
-constexpr int BCACHE = 16;
+#ifndef QLIN_BUCKET_THREADS
+#define QLIN_BUCKET_THREADS 256
+#endif
+constexpr int BUCKET_THREADS = QLIN_BUCKET_THREADS;
+constexpr int BCACHE = 4096 / BUCKET_THREADS;
 
 __global__ void __launch_bounds__(BUCKET_THREADS) bucket_kernel(const uint32_t* __restrict__ rhs, int R,
                                                                 int E, int M, int BMrows, int sorted,

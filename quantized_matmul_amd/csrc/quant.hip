@@ -13,8 +13,8 @@
 // storage dtype done on bit patterns. This file is compiled with
 // -ffp-contract=off.
 //
-// Both kernels are HBM-streaming: one thread owns one group (quantize) or
-// one packed word (dequantize).
+// All kernels are HBM-streaming: one thread owns one packed word and the
+// elements it encodes (the lanes of a group cooperate on its scale).
 
 #include "qlin_common.h"
 
@@ -102,62 +102,139 @@ __device__ __forceinline__ int floor_log2(float a) {
 }
 
 // ---------------------------------------------------------------- kernels
+//
+// Quantize: lane l of the grid owns packed word l, i.e. the PER = 32/bits
+// consecutive elements it encodes, so a wave reads 64*PER contiguous
+// elements (16-byte vector loads when w is 16-byte aligned) and writes 64
+// contiguous words. A group is g/PER adjacent lanes of one wave (the flat
+// element count is a multiple of g and a group never straddles a row, so
+// groups are whole and wave-aligned); its min/max (or amax) is combined
+// across those lanes with xor shuffles. Rounding is unchanged: every code
+// still takes one correctly rounded fp32 division and rint.
 
-template <int DT, int BITS>
-__global__ void __launch_bounds__(256) quantize_affine_kernel(
-    const void* __restrict__ w, int64_t rows, int64_t cols, int g, uint32_t* __restrict__ wq,
-    void* __restrict__ scales, void* __restrict__ biases) {
-    const int64_t groups_per_row = cols / g;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= rows * groups_per_row) return;
-    const int64_t base = gid * g;  // groups are contiguous in row-major order
-    const int n = (1 << BITS) - 1;
-
-    // plain comparisons (not fminf/fmaxf) so that the first of +0/-0 is kept
-    float lo = load_f<DT>(w, base), hi = lo;
-    for (int i = 1; i < g; ++i) {
-        float v = load_f<DT>(w, base + i);
-        lo = (v < lo) ? v : lo;
-        hi = (v > hi) ? v : hi;
-    }
-    const float z = round_down_to<DT>(lo);
-    const float range = hi - z;
-    const float s32 = __fdiv_rn(range, (float)n);
-    const float s = round_up_to<DT>(s32);
-
-    constexpr int PER = 32 / BITS;
-    uint32_t* out = wq + base / PER;
-    for (int i0 = 0; i0 < g; i0 += PER) {
-        uint32_t word = 0;
-        for (int e = 0; e < PER; ++e) {
-            uint32_t q = 0;
-            if (s != 0.0f) {
-                float d = load_f<DT>(w, base + i0 + e) - z;
-                float t = rintf(__fdiv_rn(d, s));
-                t = fminf(fmaxf(t, 0.0f), (float)n);
-                q = (uint32_t)t;
-            }
-            word |= q << (e * BITS);
+// PER elements of dtype DT starting at element i (i a multiple of PER).
+template <int DT, int PER, bool VEC>
+__device__ __forceinline__ void load_chunk(const void* w, int64_t i, float (&v)[PER]) {
+    if constexpr (!VEC) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[e] = load_f<DT>(w, i + e);
+    } else if constexpr (DT == QLIN_F32) {
+        const float4* p = (const float4*)((const float*)w + i);
+#pragma unroll
+        for (int q = 0; q < PER / 4; ++q) {
+            const float4 t = p[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
         }
-        out[i0 / PER] = word;
+    } else {
+        constexpr int NW = PER / 2;    // dwords of 16-bit elements
+        uint32_t d[NW];
+        if constexpr (NW % 4 == 0) {
+            const uint4* p = (const uint4*)((const uint16_t*)w + i);
+#pragma unroll
+            for (int q = 0; q < NW / 4; ++q) {
+                const uint4 t = p[q];
+                d[4 * q] = t.x; d[4 * q + 1] = t.y; d[4 * q + 2] = t.z; d[4 * q + 3] = t.w;
+            }
+        } else {   // NW == 2
+            const uint2 t = *(const uint2*)((const uint16_t*)w + i);
+            d[0] = t.x; d[1] = t.y;
+        }
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            if constexpr (DT == QLIN_BF16) {
+                v[2 * q] = bf16_bits_to_f32(d[q] & 0xFFFFu);
+                v[2 * q + 1] = bf16_bits_to_f32(d[q] >> 16);
+            } else {
+                v[2 * q] = f16_bits_to_f32(d[q] & 0xFFFFu);
+                v[2 * q + 1] = f16_bits_to_f32(d[q] >> 16);
+            }
+        }
     }
-    store_f<DT>(scales, gid, s);
-    store_f<DT>(biases, gid, z);
 }
 
-template <int DT, int MODE>
+// Min (MIN) or max of v over the LPG adjacent lanes of a group, LPG a power
+// of two <= 64. Each stage merges two neighbouring blocks of lanes with the
+// lower block's value as the first operand, so among equal values (+0 and
+// -0) every lane ends with the first one in element order, as a sequential
+// scan with plain comparisons keeps it.
+template <int LPG, bool MIN>
+__device__ __forceinline__ float group_minmax(float v) {
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) {
+        const float p = __shfl_xor(v, off, 64);
+        const bool low = (threadIdx.x & off) == 0;
+        const float a = low ? v : p, b = low ? p : v;   // a: lower block, b: upper block
+        v = MIN ? ((b < a) ? b : a) : ((b > a) ? b : a);
+    }
+    return v;
+}
+
+// Max of non-negative v over the LPG adjacent lanes of a group.
+template <int LPG>
+__device__ __forceinline__ float group_amax(float v) {
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+template <int DT, int BITS, bool VEC, int LPG>
+__global__ void __launch_bounds__(256) quantize_affine_kernel(
+    const void* __restrict__ w, int64_t words, int g, uint32_t* __restrict__ wq,
+    void* __restrict__ scales, void* __restrict__ biases) {
+    constexpr int PER = 32 / BITS;
+    const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = wid < words;               // whole groups are live or not
+    const int n = (1 << BITS) - 1;
+    float v[PER];
+    load_chunk<DT, PER, VEC>(w, (live ? wid : 0) * PER, v);
+
+    // group min and max; plain comparisons (not fminf/fmaxf) keep the first
+    // of +0/-0 within a lane, and the lanes are combined in element order
+    float lo = v[0], hi = v[0];
+#pragma unroll
+    for (int e = 1; e < PER; ++e) {
+        lo = (v[e] < lo) ? v[e] : lo;
+        hi = (v[e] > hi) ? v[e] : hi;
+    }
+    lo = group_minmax<LPG, true>(lo);
+    hi = group_minmax<LPG, false>(hi);
+    const float z = round_down_to<DT>(lo);
+    const float s = round_up_to<DT>(__fdiv_rn(hi - z, (float)n));
+
+    uint32_t word = 0;
+    if (s != 0.0f) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            float t = rintf(__fdiv_rn(v[e] - z, s));
+            t = fminf(fmaxf(t, 0.0f), (float)n);
+            word |= (uint32_t)t << (e * BITS);
+        }
+    }
+    if (live) {
+        wq[wid] = word;
+        if ((threadIdx.x & (LPG - 1)) == 0) {
+            const int64_t gid = wid / LPG;
+            store_f<DT>(scales, gid, s);
+            store_f<DT>(biases, gid, z);
+        }
+    }
+}
+
+template <int DT, int MODE, bool VEC, int LPG>
 __global__ void __launch_bounds__(256) quantize_micro_kernel(
-    const void* __restrict__ w, int64_t rows, int64_t cols, int g, uint32_t* __restrict__ wq,
+    const void* __restrict__ w, int64_t words, int g, uint32_t* __restrict__ wq,
     uint8_t* __restrict__ scales) {
     constexpr int BITS = (MODE == MXFP8) ? 8 : 4;
     constexpr int PER = 32 / BITS;
-    const int64_t groups_per_row = cols / g;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= rows * groups_per_row) return;
-    const int64_t base = gid * g;
+    const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = wid < words;
+    float v[PER];
+    load_chunk<DT, PER, VEC>(w, (live ? wid : 0) * PER, v);
 
     float amax = 0.0f;
-    for (int i = 0; i < g; ++i) amax = fmaxf(amax, fabsf(load_f<DT>(w, base + i)));
+#pragma unroll
+    for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = group_amax<LPG>(amax);
 
     uint32_t sbyte;
     float sc = 0.0f;  // nvfp4 element divisor
@@ -171,34 +248,32 @@ __global__ void __launch_bounds__(256) quantize_micro_kernel(
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
         sbyte = (uint32_t)(e + 127);
     }
-
-    uint32_t* out = wq + base / PER;
-    for (int i0 = 0; i0 < g; i0 += PER) {
-        uint32_t word = 0;
-        for (int k = 0; k < PER; ++k) {
-            float v = load_f<DT>(w, base + i0 + k);
-            uint32_t c;
-            if constexpr (MODE == NVFP4) {
-                c = (sc == 0.0f) ? ((__float_as_uint(v) >> 28) & 8u) : e2m1_encode(__fdiv_rn(v, sc));
-            } else if constexpr (MODE == MXFP8) {
-                c = e4m3_encode(__builtin_ldexpf(v, -e));
-            } else {
-                c = e2m1_encode(__builtin_ldexpf(v, -e));
-            }
-            word |= c << (k * BITS);
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        uint32_t c;
+        if constexpr (MODE == NVFP4) {
+            c = (sc == 0.0f) ? ((__float_as_uint(v[k]) >> 28) & 8u) : e2m1_encode(__fdiv_rn(v[k], sc));
+        } else if constexpr (MODE == MXFP8) {
+            c = e4m3_encode(__builtin_ldexpf(v[k], -e));
+        } else {
+            c = e2m1_encode(__builtin_ldexpf(v[k], -e));
         }
-        out[i0 / PER] = word;
+        word |= c << (k * BITS);
     }
-    scales[gid] = (uint8_t)sbyte;
+    if (live) {
+        wq[wid] = word;
+        if ((threadIdx.x & (LPG - 1)) == 0) scales[wid / LPG] = (uint8_t)sbyte;
+    }
 }
 
-// One thread per packed word; out row-major [rows, cols].
-template <int SDT, int ODT, int BITS, int MODE>
+// One thread per packed word; out row-major [rows, cols]. VEC: the word's
+// PER outputs go out as 16-byte (or 8-byte) vector stores.
+template <int SDT, int ODT, int BITS, int MODE, bool VEC>
 __global__ void __launch_bounds__(256) dequantize_kernel(
     const uint32_t* __restrict__ wq, const void* __restrict__ scales,
-    const void* __restrict__ biases, int64_t rows, int64_t cols, int g, void* __restrict__ out) {
+    const void* __restrict__ biases, int64_t words, int g, void* __restrict__ out) {
     constexpr int PER = 32 / BITS;
-    const int64_t words = rows * (cols / PER);
     const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (wid >= words) return;
     const int64_t k0 = wid * PER;           // flat element index of the word's first code
@@ -213,14 +288,36 @@ __global__ void __launch_bounds__(256) dequantize_kernel(
     } else {
         s = e8m0_to_f32(((const uint8_t*)scales)[gidx]);
     }
+    float v[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         uint32_t q = (word >> (e * BITS)) & ((1u << BITS) - 1u);
-        float v;
-        if constexpr (MODE == AFFINE) v = __builtin_fmaf(s, (float)q, z);
-        else if constexpr (MODE == MXFP8) v = e4m3_to_f32(q) * s;
-        else v = e2m1_to_f32(q) * s;
-        store_f<ODT>(out, k0 + e, v);
+        if constexpr (MODE == AFFINE) v[e] = __builtin_fmaf(s, (float)q, z);
+        else if constexpr (MODE == MXFP8) v[e] = e4m3_to_f32(q) * s;
+        else v[e] = e2m1_to_f32(q) * s;
+    }
+    if constexpr (!VEC) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) store_f<ODT>(out, k0 + e, v[e]);
+    } else if constexpr (ODT == QLIN_F32) {
+        float4* p = (float4*)((float*)out + k0);
+#pragma unroll
+        for (int q = 0; q < PER / 4; ++q) p[q] = float4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else {
+        uint32_t d[PER / 2];
+#pragma unroll
+        for (int q = 0; q < PER / 2; ++q) {
+            const uint32_t a = ODT == QLIN_BF16 ? f32_to_bf16_rne(v[2 * q]) : f32_to_f16_rne(v[2 * q]);
+            const uint32_t b = ODT == QLIN_BF16 ? f32_to_bf16_rne(v[2 * q + 1]) : f32_to_f16_rne(v[2 * q + 1]);
+            d[q] = a | (b << 16);
+        }
+        if constexpr (PER / 2 % 4 == 0) {
+            uint4* p = (uint4*)((uint16_t*)out + k0);
+#pragma unroll
+            for (int q = 0; q < PER / 8; ++q) p[q] = uint4{d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]};
+        } else {   // PER == 4
+            *(uint2*)((uint16_t*)out + k0) = uint2{d[0], d[1]};
+        }
     }
 }
 
@@ -238,25 +335,48 @@ inline unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
+// lanes per group: g / PER, a power of two from 1 to 32
+template <class F>
+hipError_t dispatch_lpg(int lpg, F&& f) {
+    switch (lpg) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    case 16: return f(std::integral_constant<int, 16>{});
+    case 32: return f(std::integral_constant<int, 32>{});
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int g,
                            int bits, int mode, uint32_t* wq, void* scales, void* biases,
                            hipStream_t st) {
-    const int64_t groups = rows * (cols / g);
-    const unsigned nb = nblocks(groups);
+    const int64_t words = rows * (cols * bits / 32);
+    const unsigned nb = nblocks(words);
+    const int per = 32 / bits;
+    const bool vec = ((uintptr_t)w & 15) == 0;
     return dispatch_dtype(w_dtype, [&](auto dt) -> hipError_t {
         constexpr int DT = decltype(dt)::value;
-        if (mode == AFFINE) {
-            if (bits == 2) quantize_affine_kernel<DT, 2><<<nb, 256, 0, st>>>(w, rows, cols, g, wq, scales, biases);
-            else if (bits == 4) quantize_affine_kernel<DT, 4><<<nb, 256, 0, st>>>(w, rows, cols, g, wq, scales, biases);
-            else quantize_affine_kernel<DT, 8><<<nb, 256, 0, st>>>(w, rows, cols, g, wq, scales, biases);
-        } else if (mode == MXFP4) {
-            quantize_micro_kernel<DT, MXFP4><<<nb, 256, 0, st>>>(w, rows, cols, g, wq, (uint8_t*)scales);
-        } else if (mode == MXFP8) {
-            quantize_micro_kernel<DT, MXFP8><<<nb, 256, 0, st>>>(w, rows, cols, g, wq, (uint8_t*)scales);
-        } else {
-            quantize_micro_kernel<DT, NVFP4><<<nb, 256, 0, st>>>(w, rows, cols, g, wq, (uint8_t*)scales);
-        }
-        return hipGetLastError();
+        return dispatch_lpg(g / per, [&](auto lpgc) -> hipError_t {
+            constexpr int LPG = decltype(lpgc)::value;
+            auto go = [&](auto kv) -> hipError_t {
+                constexpr bool V = decltype(kv)::value;
+                if (mode == AFFINE) {
+                    if (bits == 2) quantize_affine_kernel<DT, 2, V, LPG><<<nb, 256, 0, st>>>(w, words, g, wq, scales, biases);
+                    else if (bits == 4) quantize_affine_kernel<DT, 4, V, LPG><<<nb, 256, 0, st>>>(w, words, g, wq, scales, biases);
+                    else quantize_affine_kernel<DT, 8, V, LPG><<<nb, 256, 0, st>>>(w, words, g, wq, scales, biases);
+                } else if (mode == MXFP4) {
+                    quantize_micro_kernel<DT, MXFP4, V, LPG><<<nb, 256, 0, st>>>(w, words, g, wq, (uint8_t*)scales);
+                } else if (mode == MXFP8) {
+                    quantize_micro_kernel<DT, MXFP8, V, LPG><<<nb, 256, 0, st>>>(w, words, g, wq, (uint8_t*)scales);
+                } else {
+                    quantize_micro_kernel<DT, NVFP4, V, LPG><<<nb, 256, 0, st>>>(w, words, g, wq, (uint8_t*)scales);
+                }
+                return hipGetLastError();
+            };
+            return vec ? go(std::true_type{}) : go(std::false_type{});
+        });
     });
 }
 
@@ -265,21 +385,26 @@ hipError_t launch_dequantize(const uint32_t* wq, const void* scales, const void*
                              void* out, int out_dtype, hipStream_t st) {
     const int64_t words = rows * (cols * bits / 32);
     const unsigned nb = nblocks(words);
+    const bool vec = ((uintptr_t)out & 15) == 0;
     return dispatch_dtype(out_dtype, [&](auto odt) -> hipError_t {
         constexpr int ODT = decltype(odt)::value;
-        if (mode != AFFINE) {
-            if (mode == MXFP4) dequantize_kernel<QLIN_F32, ODT, 4, MXFP4><<<nb, 256, 0, st>>>(wq, scales, biases, rows, cols, g, out);
-            else if (mode == NVFP4) dequantize_kernel<QLIN_F32, ODT, 4, NVFP4><<<nb, 256, 0, st>>>(wq, scales, biases, rows, cols, g, out);
-            else dequantize_kernel<QLIN_F32, ODT, 8, MXFP8><<<nb, 256, 0, st>>>(wq, scales, biases, rows, cols, g, out);
-            return hipGetLastError();
-        }
-        return dispatch_dtype(sdtype, [&](auto sdt) -> hipError_t {
-            constexpr int SDT = decltype(sdt)::value;
-            if (bits == 2) dequantize_kernel<SDT, ODT, 2, AFFINE><<<nb, 256, 0, st>>>(wq, scales, biases, rows, cols, g, out);
-            else if (bits == 4) dequantize_kernel<SDT, ODT, 4, AFFINE><<<nb, 256, 0, st>>>(wq, scales, biases, rows, cols, g, out);
-            else dequantize_kernel<SDT, ODT, 8, AFFINE><<<nb, 256, 0, st>>>(wq, scales, biases, rows, cols, g, out);
-            return hipGetLastError();
-        });
+        auto go = [&](auto kv) -> hipError_t {
+            constexpr bool V = decltype(kv)::value;
+            if (mode != AFFINE) {
+                if (mode == MXFP4) dequantize_kernel<QLIN_F32, ODT, 4, MXFP4, V><<<nb, 256, 0, st>>>(wq, scales, biases, words, g, out);
+                else if (mode == NVFP4) dequantize_kernel<QLIN_F32, ODT, 4, NVFP4, V><<<nb, 256, 0, st>>>(wq, scales, biases, words, g, out);
+                else dequantize_kernel<QLIN_F32, ODT, 8, MXFP8, V><<<nb, 256, 0, st>>>(wq, scales, biases, words, g, out);
+                return hipGetLastError();
+            }
+            return dispatch_dtype(sdtype, [&](auto sdt) -> hipError_t {
+                constexpr int SDT = decltype(sdt)::value;
+                if (bits == 2) dequantize_kernel<SDT, ODT, 2, AFFINE, V><<<nb, 256, 0, st>>>(wq, scales, biases, words, g, out);
+                else if (bits == 4) dequantize_kernel<SDT, ODT, 4, AFFINE, V><<<nb, 256, 0, st>>>(wq, scales, biases, words, g, out);
+                else dequantize_kernel<SDT, ODT, 8, AFFINE, V><<<nb, 256, 0, st>>>(wq, scales, biases, words, g, out);
+                return hipGetLastError();
+            });
+        };
+        return vec ? go(std::true_type{}) : go(std::false_type{});
     });
 }
 
