@@ -93,6 +93,38 @@ def test_quantize_special_values_bit_exact():
                 assert np.array_equal(to_oracle(qw.biases), bi), (dtype, mode)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8)] + MICRO_CASES)
+def test_quantize_dequantize_unaligned_pointers(dtype, mode, g, bits):
+    """Input and output one element off a 16-byte boundary (element-wise
+    loads and stores instead of vector ones): the same bits as aligned."""
+    import ctypes
+    w, wb = gpu_weight((21, 256), 0.02, 14, dtype)
+    buf = torch.empty(w.numel() + 1, dtype=w.dtype, device=DEV)
+    wu = buf[1:].view(w.shape)
+    wu.copy_(w)
+    assert wu.data_ptr() % 16 != 0
+    qa = qm.quantize(w, g, bits, mode)
+    qu = qm.quantize(wu, g, bits, mode)
+    odt = torch.bfloat16
+    da = qm.dequantize(qa, odt)
+    obuf = torch.empty(da.numel() + 1, dtype=odt, device=DEV)
+    lib = qm.load_library()
+    vp = ctypes.c_void_p
+    rows, cols = w.shape
+    rc = lib.qlin_dequantize(vp(qa.value.data_ptr()), vp(qa.scales.data_ptr()),
+                             vp(qa.biases.data_ptr()) if qa.biases is not None else None,
+                             {torch.float32: 0, torch.bfloat16: 2, torch.float16: 1, torch.uint8: 3}[qa.scales.dtype],
+                             rows, cols, g, bits, mode.encode(), vp(obuf[1:].data_ptr()), 2,
+                             vp(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(qu.value, qa.value) and torch.equal(qu.scales.view(torch.uint8), qa.scales.view(torch.uint8))
+    if qa.biases is not None:
+        assert torch.equal(qu.biases.view(torch.uint8), qa.biases.view(torch.uint8))
+    assert torch.equal(obuf[1:].view(da.shape).view(torch.int16), da.view(torch.int16))
+
+
 # ---------------------------------------------------------------- dequantize
 
 @pytest.mark.parametrize("sdtype", ["f32", "bf16", "f16"])
