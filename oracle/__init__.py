@@ -18,6 +18,7 @@ Functions and what they follow (page titles and sections):
                       "Emily.Quantization.Layers" quantized_dense (layouts);
                       mlx-rs ``quantized_matmul`` and test_quantized_matmul.
   quantized_dense     "Emily.Quantization.Layers" quantized_dense (the bias).
+  qqmm                mlx-rs ``qqmm`` (x quantized on the fly, nvfp4/mxfp8).
   gather_qmm          "EMLX.Quantization" gather_quantized_matmul; mlx-rs
                       ``gather_qmm`` and test_gather_qmm.
 Readings of points the pages leave open are stated in ``qlin_oracle.c``.
@@ -65,10 +66,11 @@ def _load():
                                             i32, cs, vp]
     lib.oracle_quantized_dense.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i64, i32, i32,
                                            i32, cs, vp, i32, ctypes.c_double, vp]
+    lib.oracle_qqmm.argtypes = [vp, i32, i64, i64, vp, vp, i64, i32, i32, i32, cs, vp, vp]
     lib.oracle_gather_qmm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp, vp,
                                       i64, i32, i32, i32, cs, vp]
     for f in ("oracle_quantize", "oracle_dequantize", "oracle_quantized_matmul",
-              "oracle_quantized_dense", "oracle_gather_qmm"):
+              "oracle_quantized_dense", "oracle_qqmm", "oracle_gather_qmm"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -198,6 +200,29 @@ def quantized_dense(x, x_dtype, wq, scales, biases, bias=None, bias_dtype="f32",
         float(bias_value), _ptr(y))
     _check(rc, "quantized_dense")
     return y
+
+
+def qqmm(x, x_dtype, wq, scales, transpose=True, group_size=16, bits=4, mode="nvfp4",
+         return_xhat=False):
+    """y (float64) = dequant(quantize(x)) . dequant(W)^T (or . dequant(W)),
+    x quantized along its last axis with W's microscaled mode (nvfp4 or
+    mxfp8). With return_xhat, also dequant(quantize(x)) as float32."""
+    x = np.ascontiguousarray(x)
+    wq = np.ascontiguousarray(wq)
+    if transpose:
+        N, K = wq.shape[0], wq.shape[1] * 32 // bits
+    else:
+        K, N = wq.shape[0], wq.shape[1] * 32 // bits
+    M = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    if x.shape[-1] != K:
+        raise OracleError("x's last dim does not match W")
+    y = np.zeros(x.shape[:-1] + (N,), np.float64)
+    xhat = np.zeros(x.shape, np.float32)
+    rc = _load().oracle_qqmm(_ptr(x), DTYPES[x_dtype], M, K, _ptr(wq),
+                             _ptr(np.ascontiguousarray(scales)), N, int(bool(transpose)),
+                             group_size, bits, mode.encode(), _ptr(xhat), _ptr(y))
+    _check(rc, "qqmm")
+    return (y, xhat) if return_xhat else y
 
 
 def gather_qmm(x, x_dtype, wq, scales, biases, rhs_indices, lhs_indices=None, transpose=True,

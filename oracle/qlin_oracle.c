@@ -517,6 +517,40 @@ int oracle_quantized_dense(const void* x, int x_dtype, int64_t M, int64_t K, con
     return OR_OK;
 }
 
+/* qqmm ([RS] qqmm doc comment: x is quantized on the fly, W arrives already
+ * quantized; the modes are nvfp4 and mxfp8): y = dequant(quantize(x)) .
+ * dequant(W)^T (transpose) or dequant(quantize(x)) . dequant(W).
+ * READINGS: x is quantized along its last axis by this file's microscaled
+ * rule (the one that quantizes weights) with W's mode, group size and bits;
+ * the optional global scales the page passes empty are absent (one level of
+ * scales). xhat, if not NULL, receives dequant(quantize(x)) in fp32 (every
+ * value is exact there); y is fp64. */
+int oracle_qqmm(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* wq,
+                const void* scales, int64_t N, int transpose, int group_size, int bits,
+                const char* mode_str, float* xhat, double* y) {
+    int mode = parse_mode(mode_str);
+    if (mode != MODE_NVFP4 && mode != MODE_MXFP8) return OR_EINVAL;
+    if (check_params(mode, group_size, bits, K) != OR_OK) return OR_EINVAL;
+    if (check_params(mode, group_size, bits, transpose ? K : N) != OR_OK) return OR_EINVAL;
+    if (!x || !wq || !scales || !y || M < 0 || N <= 0 || K <= 0) return OR_EINVAL;
+    if (dtype_fmt(x_dtype) < 0) return OR_EINVAL;
+    if (M == 0) return OR_OK;
+    uint32_t* xq = (uint32_t*)malloc((size_t)(M * K * bits / 32) * sizeof(uint32_t));
+    uint8_t* xs = (uint8_t*)malloc((size_t)(M * K / group_size));
+    float* xd = (float*)malloc((size_t)(M * K) * sizeof(float));
+    int rc = (xq && xs && xd) ? OR_OK : OR_EUNSUP;
+    if (rc == OR_OK) rc = oracle_quantize(x, x_dtype, M, K, group_size, bits, mode_str, xq, xs, NULL);
+    if (rc == OR_OK) rc = oracle_dequantize(xq, xs, NULL, OR_U8, M, K, group_size, bits, mode_str,
+                                            xd, OR_F32);
+    if (rc == OR_OK) rc = oracle_quantized_matmul(xd, OR_F32, M, K, wq, scales, NULL, OR_U8, N,
+                                                  transpose, group_size, bits, mode_str, y);
+    if (rc == OR_OK && xhat) memcpy(xhat, xd, (size_t)(M * K) * sizeof(float));
+    free(xq);
+    free(xs);
+    free(xd);
+    return rc;
+}
+
 /* gather_qmm ([EMLX] gather_quantized_matmul; [RS] gather_qmm doc and
  * test_gather_qmm): x [B, M, K], W stacked [E, N, K] (transpose) or
  * [E, K, N]; for each r, y[r] = x[lhs[r]] . dequant(W[rhs[r]])^T, with

@@ -452,6 +452,88 @@ def test_dense_rejects_bad_bias():
         oracle.quantized_dense(x, "bf16", wq, sc, bi, None, bias_value=1e39, group_size=32, bits=4)
 
 
+# ------------------------------------------------------------------ qqmm
+# mlx-rs qqmm: x quantized on the fly (nvfp4 or mxfp8), W already quantized.
+
+def _micro_grid_x(mode, rows, K, seed):
+    """x whose groups are already on the mode's grid: code values times a
+    chosen scale with the group maximum present (quantize reproduces it)."""
+    g, bits = oracle.MODE_PAIRING[mode]
+    r = np.random.default_rng(seed)
+    fmt = "e4m3" if mode == "mxfp8" else "e2m1"
+    valid = [c for c in range(1 << bits) if not (fmt == "e4m3" and (c & 0x7F) == 0x7F)]
+    codes = r.choice(valid, size=(rows, K))
+    codes[:, ::g] = 0x7E if fmt == "e4m3" else 0x7
+    vals = np.vectorize(lambda c: oracle.decode(fmt, int(c)))(codes)
+    G = K // g
+    if mode == "nvfp4":
+        scale = np.vectorize(lambda c: oracle.decode("e4m3", int(c)))(r.integers(0x28, 0x48, size=(rows, G)))
+    else:
+        scale = 2.0 ** r.integers(-6, 3, size=(rows, G))
+    return (vals * scale.repeat(g, 1)).astype(np.float32)
+
+
+def _micro_weight(mode, N, K, seed):
+    g, bits = oracle.MODE_PAIRING[mode]
+    tw, wb = synth.normal((N, K), 0.02, seed, synth.WEIGHT, "bf16")
+    wq, sc, _ = oracle.quantize(wb, "bf16", g, bits, mode)
+    return wq, sc, g, bits
+
+
+@pytest.mark.parametrize("mode", ["nvfp4", "mxfp8"])
+def test_qqmm_grid_x_equals_quantized_matmul(mode):
+    """x already on its grid: quantizing it changes nothing, so qqmm is the
+    plain quantized matmul of x, exactly."""
+    N, K, M = 24, 128, 5
+    x = _micro_grid_x(mode, M, K, seed=90)
+    wq, sc, g, bits = _micro_weight(mode, N, K, 90)
+    y, xhat = oracle.qqmm(x, "f32", wq, sc, True, g, bits, mode, return_xhat=True)
+    assert np.array_equal(xhat, x)
+    assert np.array_equal(y, oracle.quantized_matmul(x, "f32", wq, sc, None, True, g, bits, mode))
+
+
+@pytest.mark.parametrize("mode,k", [("nvfp4", 3), ("nvfp4", -2), ("mxfp8", 5), ("mxfp8", -7)])
+def test_qqmm_power_of_two_scaling(mode, k):
+    """Scaling x by 2^k moves every block scale by 2^k and keeps the codes
+    (no scale leaves its normal range here), so y scales exactly."""
+    N, K, M = 16, 128, 4
+    tx, _ = synth.normal((M, K), 1.0, 91, synth.ACT, "f32")
+    x = tx.numpy()
+    wq, sc, g, bits = _micro_weight(mode, N, K, 91)
+    y = oracle.qqmm(x, "f32", wq, sc, True, g, bits, mode)
+    y2 = oracle.qqmm((x * 2.0 ** k).astype(np.float32), "f32", wq, sc, True, g, bits, mode)
+    assert np.array_equal(y2, y * 2.0 ** k)
+
+
+@pytest.mark.parametrize("mode", ["nvfp4", "mxfp8"])
+def test_qqmm_error_bound_against_unquantized_x(mode):
+    """Each x element moves by at most half a grid step of its group (closed
+    form below); y moves by at most the sum of those moves times |W|."""
+    N, K, M = 16, 256, 3
+    tx, _ = synth.normal((M, K), 1.0, 92, synth.ACT, "f32")
+    x = tx.numpy().astype(np.float64)
+    wq, sc, g, bits = _micro_weight(mode, N, K, 92)
+    y, xhat = oracle.qqmm(tx.numpy(), "f32", wq, sc, True, g, bits, mode, return_xhat=True)
+    amax = np.abs(x).reshape(M, K // g, g).max(-1).repeat(g, 1)
+    if mode == "mxfp8":   # e4m3 under the shared exponent e = floor(log2 amax) - 8: half an ulp
+        E = np.floor(np.log2(amax))   # of the top binade, or the clamp of (448, 512) x 2^e to 448
+        bound_x = np.maximum(2.0 ** (E - 4), amax - 448.0 * 2.0 ** (E - 8))
+    else:                 # e2m1 grid gap <= 2 at scale ~amax/6 (scale rounded up to 2^-4 relative)
+        bound_x = amax / 6.0 * (1 + 2.0 ** -4)
+    assert np.all(np.abs(xhat - x) <= bound_x)
+    wd = oracle.dequantize(wq, sc, None, g, bits, mode).astype(np.float64)
+    y0 = oracle.quantized_matmul(tx.numpy(), "f32", wq, sc, None, True, g, bits, mode)
+    assert np.all(np.abs(y - y0) <= bound_x @ np.abs(wd).T + 1e-9)
+
+
+def test_qqmm_modes():
+    wq, sc, g, bits = _micro_weight("mxfp8", 8, 64, 93)
+    x = np.zeros((2, 64), np.float32)
+    for mode, gg, b in [("affine", 64, 4), ("mxfp4", 32, 4)]:
+        with pytest.raises(oracle.OracleError):
+            oracle.qqmm(x, "f32", wq, sc, True, gg, b, mode)
+
+
 def test_page_example_shapes():
     # "Emily.QuantizedWeight" from_dense / to_dense examples
     t, w = synth.iota((4, 64))
