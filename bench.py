@@ -231,6 +231,32 @@ def main():
         torch.cuda.empty_cache()
         return res
 
+    def qqmm_case(M, N, K, mode, wid=501):
+        """qqmm: x quantized on the fly (one launch into the workspace) then the
+        microscaled matmul; weight copies cycled like the decode cases."""
+        g, bits = {"mxfp8": (32, 8), "nvfp4": (16, 4)}[mode]
+        qw = make_weight((N, K), wid, mode, g, bits, True)
+        per = qw_bytes(qw)
+        ncopy = max(1, math.ceil(ROTATE_BYTES / per)) if M <= 16 else 1
+        copies = [qw] + [clone_qw(qw) for _ in range(ncopy - 1)]
+        x, _ = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
+        x = x.to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(qm.qqmm_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+        fns = [lambda c=c: qm.qqmm(x, c, workspace=ws, out=y) for c in copies]
+        n = max(len(fns), (max(16, args.steps // (4 if M <= 16 else 8)) // len(fns)) * len(fns))
+        sec = timed(fns, n, min(args.warmup, 5))
+        # algorithmic bytes: W, its scales, x read once, y written once
+        alg = per + x.numel() * 2 + y.numel() * 2
+        flops = 2 * M * N * K
+        del copies, fns
+        torch.cuda.empty_cache()
+        return {"workload": f"qqmm {mode} (x quantized on the fly) M{M} N{N} K{K} transpose=true",
+                "us": sec * 1e6, "GB/s": alg / sec / 1e9, "frac_hbm": alg / sec / 1e9 / HBM_PEAK_GBS,
+                "TFLOP/s": flops / sec / 1e12,
+                "frac_mfma": flops / sec / 1e12 / MFMA_PEAK_TFLOPS["bf16"], "alg_bytes": alg,
+                "copies": ncopy, "steps": n}
+
     def moe_case(sorted_indices, T=512, wid=301):
         """gather_qmm over 64 stacked experts, T tokens x top-8 distinct experts;
         cycles through >= 512 MB of weight copies like the decode cases."""
@@ -311,6 +337,11 @@ def main():
     if args.only == "all":
         for (N, K, bits, g, mode) in [(14336, 4096, 4, 64, "affine"), (8192, 8192, 4, 32, "mxfp4")]:
             for r in quant_case(N, K, bits, g, mode):
+                results.append(r)
+                log(json.dumps(r))
+        for mode in ("mxfp8", "nvfp4"):
+            for M in (1, 512):
+                r = qqmm_case(M, 8192, 8192, mode)
                 results.append(r)
                 log(json.dumps(r))
         for s in (False, True):

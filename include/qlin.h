@@ -150,6 +150,35 @@ qlin_status qlin_quantized_dense(const void* x, qlin_dtype x_dtype, int64_t M, i
                                  void* stream);
 
 /*
+ * qlin_qqmm_workspace_bytes -- device workspace qlin_qqmm needs for x [M, K]:
+ * the decoded activation, M*K bf16 values.
+ */
+size_t qlin_qqmm_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * qlin_qqmm -- matmul with both operands quantized: x is quantized on the
+ * fly, W arrives quantized (mlx-rs qqmm: the nvfp4 and mxfp8 modes; the
+ * optional global scales are not taken -- one level of scales).
+ *   x        bf16 [M, K]; quantized along K with W's mode, group size and
+ *            bits by the same rule as qlin_quantize, then decoded back into
+ *            the workspace (every decoded value is exact in bf16).
+ *   wq, scales  W as for qlin_quantized_matmul in mode "nvfp4" (16, 4) or
+ *            "mxfp8" (32, 8); no biases. transpose as there.
+ *   workspace   device memory of at least qlin_qqmm_workspace_bytes(M, K)
+ *            bytes, 16-byte aligned; the caller owns it; overwritten.
+ *   y        out, bf16 [M, N] = dequant(quantize(x)) . dequant(W)^T (or . W),
+ *            fp32 accumulation.
+ * Errors: QLIN_ERR_INVALID_ARGUMENT for another mode, a mode/group/bits
+ * mismatch, K not a multiple of the group, a short or misaligned workspace,
+ * NULL pointers; QLIN_ERR_UNSUPPORTED for x other than bf16. M == 0 is a
+ * no-op.
+ */
+qlin_status qlin_qqmm(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, const uint32_t* wq,
+                      const void* scales, int64_t N, int transpose, int group_size, int bits,
+                      const char* mode, void* workspace, size_t workspace_bytes, void* y,
+                      void* stream);
+
+/*
  * qlin_gather_qmm_workspace_bytes -- device workspace qlin_gather_qmm needs
  * for R index rows over E experts (bucket offsets, counts and the row
  * permutation). Always > 0.

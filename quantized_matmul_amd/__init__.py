@@ -8,7 +8,7 @@ library is not built, every call raises.
 
 Raw ABI calls (same names as the C functions, minus the ``qlin_`` prefix):
 ``quantize``, ``dequantize``, ``quantized_matmul``, ``quantized_dense``,
-``gather_qmm`` operate on explicit tensors. ``QuantizedWeight`` bundles the packed weight with its
+``qqmm``, ``gather_qmm`` operate on explicit tensors. ``QuantizedWeight`` bundles the packed weight with its
 metadata, mirroring the field set of the "Emily.QuantizedWeight" page
 (value, scales, biases, group_size, bits, transpose, mode).
 """
@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     library_path,
     load_library,
     quantize,
+    qqmm,
+    qqmm_workspace_bytes,
     quantized_dense,
     quantized_matmul,
     MODE_DEFAULTS,

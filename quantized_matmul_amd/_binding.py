@@ -54,6 +54,10 @@ def load_library():
                                          cs, vp, i32, ctypes.c_double, vp, vp]
     lib.qlin_gather_qmm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp, vp,
                                     i64, i32, i32, i32, cs, i32, vp, sz, vp, vp]
+    lib.qlin_qqmm.argtypes = [vp, i32, i64, i64, vp, vp, i64, i32, i32, i32, cs, vp, sz, vp, vp]
+    lib.qlin_qqmm.restype = i32
+    lib.qlin_qqmm_workspace_bytes.argtypes = [i64, i64]
+    lib.qlin_qqmm_workspace_bytes.restype = sz
     lib.qlin_gather_qmm_workspace_bytes.argtypes = [i64, i64]
     lib.qlin_gather_qmm_workspace_bytes.restype = sz
     lib.qlin_last_error.restype = ctypes.c_char_p
@@ -224,6 +228,39 @@ def quantized_dense(x: torch.Tensor, qw: QuantizedWeight, bias=0,
                                   _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype], N,
                                   int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),
                                   _ptr(bias_t), bias_dt, bias_value, _ptr(y), _stream(dev))
+    _check(rc)
+    return y
+
+
+def qqmm_workspace_bytes(M: int, K: int) -> int:
+    return int(load_library().qlin_qqmm_workspace_bytes(M, K))
+
+
+def qqmm(x: torch.Tensor, qw: QuantizedWeight, workspace: Optional[torch.Tensor] = None,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qlin_qqmm (mlx-rs qqmm): bf16 x quantized on the fly with qw's mode
+    (nvfp4 or mxfp8), times the quantized weight. x [..., K] -> y [..., N]."""
+    lib = load_library()
+    dev = _dev(x)
+    _dev(qw.value)
+    if qw.value.dim() != 2:
+        raise ValueError("qqmm takes a 2-D quantized weight")
+    per = 32 // qw.bits
+    if qw.transpose:
+        N, K = qw.value.shape[0], qw.value.shape[1] * per
+    else:
+        K, N = qw.value.shape[0], qw.value.shape[1] * per
+    if x.shape[-1] != K:
+        raise ValueError(f"x's last dim {x.shape[-1]} does not match the weight's K={K}")
+    M = x.numel() // K if K else 0
+    need = qqmm_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    y = _out(out, tuple(x.shape[:-1]) + (N,), x.dtype, dev)
+    rc = lib.qlin_qqmm(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value), _ptr(qw.scales), N,
+                       int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),
+                       _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(y),
+                       _stream(dev))
     _check(rc)
     return y
 

@@ -238,6 +238,57 @@ qlin_status qlin_quantized_dense(const void* x, qlin_dtype x_dtype, int64_t M, i
                      bits, mode, ob, y, stream);
 }
 
+size_t qlin_qqmm_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 0) M = 0;
+    if (K < 0) K = 0;
+    return (size_t)M * (size_t)K * 2u;   // the decoded bf16 x
+}
+
+qlin_status qlin_qqmm(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, const uint32_t* wq,
+                      const void* scales, int64_t N, int transpose, int group_size, int bits,
+                      const char* mode, void* workspace, size_t workspace_bytes, void* y,
+                      void* stream) {
+    int m;
+    if (N <= 0 || K <= 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "N and K must be positive");
+    qlin_status st = check_mode(mode, group_size, bits, transpose ? K : N, &m);
+    if (st) return st;
+    if (m != qlin::NVFP4 && m != qlin::MXFP8)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "qqmm takes the nvfp4 and mxfp8 modes");
+    if (K % group_size != 0)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "x is quantized along K: K must be a multiple of group_size");
+    if (x_dtype != QLIN_BF16) return fail(QLIN_ERR_UNSUPPORTED, "qqmm takes bf16 x");
+    if (M < 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "M must be >= 0");
+    if (M == 0) return ok();
+    if (!x || !wq || !scales || !y) return fail(QLIN_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
+    const size_t need = qlin_qqmm_workspace_bytes(M, K);
+    if (!workspace || workspace_bytes < need)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace_bytes);
+    if (((uintptr_t)workspace & 15) != 0)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31))
+        return fail(QLIN_ERR_UNSUPPORTED, "dimensions above 2^31 are not supported");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = qlin::launch_qdq_micro(x, M, K, group_size, m, workspace, s);
+    if (e != hipSuccess) return device_status(e, "qqmm (activation quantization)");
+    qlin::QmmArgs a{};
+    a.x = workspace;
+    a.wq = wq;
+    a.scales = scales;
+    a.biases = nullptr;
+    a.y = y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.x_dtype = QLIN_BF16;
+    a.scale_dtype = QLIN_U8;
+    a.transpose = transpose ? 1 : 0;
+    a.group_size = group_size;
+    a.bits = bits;
+    a.mode = m;
+    return run_qmm(a, nullptr, nullptr, s);
+}
+
 size_t qlin_gather_qmm_workspace_bytes(int64_t R, int64_t E) {
     if (R < 0) R = 0;
     if (E < 0) E = 0;

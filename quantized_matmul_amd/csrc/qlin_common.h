@@ -131,6 +131,10 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t col
 hipError_t launch_dequantize(const uint32_t* wq, const void* scales, const void* biases,
                              int sdtype, int64_t rows, int64_t cols, int g, int bits, int mode,
                              void* out, int out_dtype, hipStream_t s);
+// qqmm's activation step: bf16 x [rows, cols] quantized with a microscaled
+// mode (MXFP8 or NVFP4, group g along cols) and decoded back into bf16 xhat.
+hipError_t launch_qdq_micro(const void* x, int64_t rows, int64_t cols, int g, int mode,
+                           void* xhat, hipStream_t s);
 // fp32 VALU path: any dtype, layout and mode; gather form if a.R > 0.
 hipError_t launch_qmm_generic(const QmmArgs& a, hipStream_t s);
 // MFMA small-M path (M <= 16, transpose, bf16 x). Returns hipErrorNotSupported

@@ -220,6 +220,43 @@ __global__ void __launch_bounds__(256) quantize_affine_kernel(
     }
 }
 
+// Block scale of a microscaled group from its amax ("Emily.QuantizedWeight",
+// Microscaled modes; OCP MX shared exponent for mx*, E4M3(amax/6) for
+// nvfp4): the scale byte, and the divisor (nvfp4) or exponent (mx*) the
+// elements are encoded with.
+template <int MODE>
+struct MicroScale {
+    uint32_t sbyte;
+    float sc;   // nvfp4 element divisor
+    int e;      // mx shared exponent
+};
+template <int MODE>
+__device__ __forceinline__ MicroScale<MODE> micro_scale(float amax) {
+    MicroScale<MODE> m{0u, 0.0f, 0};
+    if constexpr (MODE == NVFP4) {
+        m.sbyte = e4m3_encode(__fdiv_rn(amax, 6.0f));
+        m.sc = e4m3_to_f32(m.sbyte);
+    } else {
+        constexpr int EMAX_ELEM = (MODE == MXFP8) ? 8 : 2;
+        int e = (amax == 0.0f) ? -127 : floor_log2(amax) - EMAX_ELEM;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        m.e = e;
+        m.sbyte = (uint32_t)(e + 127);
+    }
+    return m;
+}
+
+// Element code of v under the group's scale.
+template <int MODE>
+__device__ __forceinline__ uint32_t micro_encode(float v, const MicroScale<MODE>& m) {
+    if constexpr (MODE == NVFP4)
+        return (m.sc == 0.0f) ? ((__float_as_uint(v) >> 28) & 8u) : e2m1_encode(__fdiv_rn(v, m.sc));
+    else if constexpr (MODE == MXFP8)
+        return e4m3_encode(__builtin_ldexpf(v, -m.e));
+    else
+        return e2m1_encode(__builtin_ldexpf(v, -m.e));
+}
+
 template <int DT, int MODE, bool VEC, int LPG>
 __global__ void __launch_bounds__(256) quantize_micro_kernel(
     const void* __restrict__ w, int64_t words, int g, uint32_t* __restrict__ wq,
@@ -234,36 +271,56 @@ __global__ void __launch_bounds__(256) quantize_micro_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = group_amax<LPG>(amax);
-
-    uint32_t sbyte;
-    float sc = 0.0f;  // nvfp4 element divisor
-    int e = 0;        // mx shared exponent
-    if constexpr (MODE == NVFP4) {
-        sbyte = e4m3_encode(__fdiv_rn(amax, 6.0f));
-        sc = e4m3_to_f32(sbyte);
-    } else {
-        constexpr int EMAX_ELEM = (MODE == MXFP8) ? 8 : 2;
-        e = (amax == 0.0f) ? -127 : floor_log2(amax) - EMAX_ELEM;
-        e = e < -127 ? -127 : (e > 127 ? 127 : e);
-        sbyte = (uint32_t)(e + 127);
-    }
+    const MicroScale<MODE> m = micro_scale<MODE>(group_amax<LPG>(amax));
     uint32_t word = 0;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        uint32_t c;
-        if constexpr (MODE == NVFP4) {
-            c = (sc == 0.0f) ? ((__float_as_uint(v[k]) >> 28) & 8u) : e2m1_encode(__fdiv_rn(v[k], sc));
-        } else if constexpr (MODE == MXFP8) {
-            c = e4m3_encode(__builtin_ldexpf(v[k], -e));
-        } else {
-            c = e2m1_encode(__builtin_ldexpf(v[k], -e));
-        }
-        word |= c << (k * BITS);
-    }
+    for (int k = 0; k < PER; ++k) word |= micro_encode<MODE>(v[k], m) << (k * BITS);
     if (live) {
         wq[wid] = word;
-        if ((threadIdx.x & (LPG - 1)) == 0) scales[wid / LPG] = (uint8_t)sbyte;
+        if ((threadIdx.x & (LPG - 1)) == 0) scales[wid / LPG] = (uint8_t)m.sbyte;
+    }
+}
+
+// qqmm's activation step (mlx-rs qqmm: x is quantized on the fly): bf16 x
+// quantized along its rows with a microscaled mode and decoded straight
+// back, xhat = decode(code) * decode(scale byte). Every such value is exact
+// in bf16 (at most 6 significant bits), so the matmul kernels then take
+// xhat as an ordinary bf16 activation. Lanes and groups as in quantize.
+template <int MODE, bool VEC, int LPG>
+__global__ void __launch_bounds__(256) qdq_micro_kernel(const void* __restrict__ x, int64_t words,
+                                                        uint16_t* __restrict__ xhat) {
+    constexpr int BITS = (MODE == MXFP8) ? 8 : 4;
+    constexpr int PER = 32 / BITS;
+    const int64_t wid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = wid < words;
+    float v[PER];
+    load_chunk<QLIN_BF16, PER, VEC>(x, (live ? wid : 0) * PER, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    const MicroScale<MODE> m = micro_scale<MODE>(group_amax<LPG>(amax));
+    const float s = MODE == NVFP4 ? e4m3_to_f32(m.sbyte) : e8m0_to_f32(m.sbyte);
+    uint32_t d[PER / 2];
+#pragma unroll
+    for (int k = 0; k < PER; k += 2) {
+        const uint32_t c0 = micro_encode<MODE>(v[k], m), c1 = micro_encode<MODE>(v[k + 1], m);
+        const float f0 = (MODE == MXFP8 ? e4m3_to_f32(c0) : e2m1_to_f32(c0)) * s;
+        const float f1 = (MODE == MXFP8 ? e4m3_to_f32(c1) : e2m1_to_f32(c1)) * s;
+        d[k / 2] = f32_to_bf16_rne(f0) | (f32_to_bf16_rne(f1) << 16);
+    }
+    if (!live) return;
+    if constexpr (VEC) {
+        if constexpr (PER == 8) {
+            *(uint4*)(xhat + wid * PER) = uint4{d[0], d[1], d[2], d[3]};
+        } else {
+            *(uint2*)(xhat + wid * PER) = uint2{d[0], d[1]};
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < PER / 2; ++k) {
+            xhat[wid * PER + 2 * k] = (uint16_t)(d[k] & 0xFFFFu);
+            xhat[wid * PER + 2 * k + 1] = (uint16_t)(d[k] >> 16);
+        }
     }
 }
 
@@ -377,6 +434,25 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t col
             };
             return vec ? go(std::true_type{}) : go(std::false_type{});
         });
+    });
+}
+
+hipError_t launch_qdq_micro(const void* x, int64_t rows, int64_t cols, int g, int mode,
+                           void* xhat, hipStream_t st) {
+    const int bits = mode == MXFP8 ? 8 : 4;
+    const int64_t words = rows * (cols * bits / 32);
+    const unsigned nb = nblocks(words);
+    const bool vec = (((uintptr_t)x | (uintptr_t)xhat) & 15) == 0;
+    return dispatch_lpg(g / (32 / bits), [&](auto lpgc) -> hipError_t {
+        constexpr int LPG = decltype(lpgc)::value;
+        auto go = [&](auto kv) -> hipError_t {
+            constexpr bool V = decltype(kv)::value;
+            if (mode == MXFP8) qdq_micro_kernel<MXFP8, V, LPG><<<nb, 256, 0, st>>>(x, words, (uint16_t*)xhat);
+            else if (mode == NVFP4) qdq_micro_kernel<NVFP4, V, LPG><<<nb, 256, 0, st>>>(x, words, (uint16_t*)xhat);
+            else return hipErrorInvalidValue;
+            return hipGetLastError();
+        };
+        return vec ? go(std::true_type{}) : go(std::false_type{});
     });
 }
 

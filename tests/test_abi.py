@@ -119,6 +119,32 @@ def test_quantized_dense_rejects(lib):
     assert call(x=None, M=0, wq=None, s=None, y=None, bias=FAKE, bdt=BF16) == 0
 
 
+def test_qqmm_rejects(lib):
+    q = lib.qlin_qqmm
+    need = lib.qlin_qqmm_workspace_bytes(2, 128)
+    assert need == 2 * 128 * 2
+    WS = ctypes.c_void_p(0x2000)
+    base = dict(x=FAKE, xdt=BF16, M=2, K=128, wq=FAKE, s=FAKE, N=64, t=1, g=32, bits=8,
+                mode=b"mxfp8", ws=WS, wsb=need, y=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return q(*a.values())
+
+    assert call(mode=b"mxfp4", g=32, bits=4) == INVALID      # nvfp4 and mxfp8 only
+    assert "nvfp4" in err(lib)
+    assert call(mode=b"affine", g=64, bits=4) == INVALID
+    assert call(mode=b"nvfp4", g=32, bits=4) == INVALID      # pairing
+    assert call(xdt=F32) == UNSUPPORTED                      # bf16 x only
+    assert call(wsb=need - 1) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(ws=ctypes.c_void_p(0x2008)) == INVALID       # 16-byte alignment
+    assert call(t=0, N=100) == INVALID                       # [K, N] groups run along N
+    assert call(t=0, K=100, N=64) == INVALID                 # x's groups run along K
+    assert call(x=None) == INVALID
+    assert call(M=0, x=None, ws=None, wsb=0) == 0            # empty: no-op
+
+
 def test_gather_rejects(lib):
     g = lib.qlin_gather_qmm
     need = lib.qlin_gather_qmm_workspace_bytes(8, 4)

@@ -542,3 +542,46 @@ def test_quantized_dense_zero_bias_is_quantized_matmul():
     x = xt.to(DEV)
     assert torch.equal(qm.quantized_dense(x, qw, 0).view(torch.int16),
                        qm.quantized_matmul(x, qw).view(torch.int16))
+
+
+# ---------------------------------------------------------------- qqmm
+# mlx-rs qqmm: x quantized on the fly (nvfp4 / mxfp8), W already quantized.
+# The decoded x is exact in bf16 and the products of decoded values are exact
+# in fp32, so the GPU result is the oracle's up to fp32 accumulation order and
+# the bf16 rounding of y: normwise 4e-3 (2^-9 rounding plus accumulation),
+# tighter than the 2e-2 bar for bf16 outputs.
+
+QQMM_CASES = [
+    # M, N, K, mode, transpose, forced path
+    (1, 512, 1024, "mxfp8", True, "decode"),
+    (1, 500, 1024, "nvfp4", True, "decode"),
+    (16, 256, 8192, "nvfp4", True, "decode"),     # direct x fragments
+    (5, 1024, 512, "mxfp8", False, "decode"),     # [in, out] kernel
+    (300, 384, 512, "mxfp8", True, "prefill"),
+    (260, 256, 512, "nvfp4", True, "prefill"),
+    (7, 128, 256, "nvfp4", True, "generic"),
+]
+
+
+@pytest.mark.parametrize("case", QQMM_CASES, ids=lambda c: f"M{c[0]}N{c[1]}K{c[2]}{c[3]}t{int(c[4])}{c[5]}")
+def test_qqmm(case):
+    M, N, K, mode, transpose, path = case
+    g, bits = oracle.MODE_PAIRING[mode]
+    w, wb = gpu_weight((N, K) if transpose else (K, N), 0.02, 51, "bf16")
+    xt, xb = synth.normal((M, K), 1.0, 51, synth.ACT, "bf16")
+    qw, (wq, sc, _) = quantize_both(w, wb, "bf16", g, bits, mode, transpose)
+    ws = torch.empty(qm.qqmm_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    os.environ["QLIN_FORCE_PATH"] = path
+    y = qm.qqmm(xt.to(DEV), qw, workspace=ws)
+    torch.cuda.synchronize()
+    os.environ.pop("QLIN_FORCE_PATH", None)
+    yref, xhat = oracle.qqmm(xb, "bf16", wq, sc, transpose, g, bits, mode, return_xhat=True)
+    # the decoded activation in the workspace, bit for bit
+    xh_bits = torch.from_numpy(xhat).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(torch.from_numpy(xhat).to(torch.bfloat16).float().numpy(), xhat)
+    assert np.array_equal(to_oracle(ws.view(torch.bfloat16).view(M, K)), xh_bits)
+    assert y.shape == (M, N) and y.dtype == torch.bfloat16
+    err = normwise_rel_err(y, yref)
+    print(f"qqmm {case}: err {err:.3e}", flush=True)
+    assert err <= 4e-3
+
