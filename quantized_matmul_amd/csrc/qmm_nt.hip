@@ -39,12 +39,16 @@ struct NtArgs {
 // row k = RPS * step + rr: one wave load covers RPS = 64 / WPB rows x WPB
 // words. The NW waves of a workgroup split K. Each lane keeps RING2 steps
 // (word, scale, bias) in flight: 16 for up to 2 activation rows of affine
-// codes, fewer otherwise (the accumulators and decoding take the
-// registers). MR = activation rows rounded up (<= 8).
+// codes (32 for one row), fewer otherwise (the accumulators and decoding
+// take the registers). MR = activation rows rounded up (<= 8).
 template <int MODE, int BITS, int G, int MR, int WPB, int NW>
 __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
-    // steps in flight per lane (microscaled decoding needs more registers)
-    constexpr int RING2 = (MR <= 2 && MODE == AFFINE) ? 16 : (MR <= 4 ? 8 : 4);
+    // steps in flight per lane (microscaled decoding needs more registers):
+    // the kernel is bound by the bytes each lane keeps in flight, so one
+    // activation row of 4- or 8-bit affine codes takes 32 (126 registers, no
+    // spills; 25 -> 22.8 us at M1), two rows 16
+    constexpr int RING2 = (MR == 1 && MODE == AFFINE && BITS >= 4) ? 32
+                        : (MR <= 2 && MODE == AFFINE) ? 16 : (MR <= 4 ? 8 : 4);
     constexpr int NWAVES = NW;
     constexpr int RPS = 64 / WPB;                     // rows per step
     constexpr int PER = 32 / BITS;
@@ -202,7 +206,11 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
         }
     __syncthreads();
     float* red = (float*)smem;  // [NWAVES][WPB][PER] per activation row
-    for (int m = 0; m < a.M && m < MR; ++m) {
+    // unrolled over the kernel's rows so acc[m] is a register, not a
+    // dynamically indexed (scratch) array; rows past M stop (uniformly)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m >= a.M) break;
         if (rr == 0) {
 #pragma unroll
             for (int e = 0; e < PER; ++e) red[(wv * WPB + cl) * PER + e] = acc[m][e];
