@@ -349,11 +349,11 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
 
 // One workgroup: per-expert counts, exclusive scan into offsets and row-tile
 // prefix, then rows placed into expert order (or the identity when the
-// caller's indices are verified non-decreasing). Four waves; each thread
+// caller's indices are verified non-decreasing). Eight waves; each thread
 // keeps the experts of its first BCACHE rows in registers, so rhs is read
 // once (the kernel is latency-bound: a few barriers and memory round trips).
 #ifndef QLIN_BUCKET_THREADS
-#define QLIN_BUCKET_THREADS 256
+#define QLIN_BUCKET_THREADS 512   // 8 waves: MoE 4096 rows ~1.8 us faster than 4
 #endif
 constexpr int BUCKET_THREADS = QLIN_BUCKET_THREADS;
 constexpr int BCACHE = 4096 / BUCKET_THREADS;
