@@ -23,6 +23,7 @@
 
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 namespace qlin {
@@ -564,6 +565,22 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
 #endif
 
 
+// Launch one kernel with `shm` bytes of dynamic LDS; the attribute that
+// allows more than the default is set once per kernel (an atomic flag each,
+// so concurrent callers at worst set it twice).
+template <auto KERN>
+hipError_t launch_with_lds(const PrefillArgs& t, int grid, int threads, size_t shm, hipStream_t st) {
+    static std::atomic<bool> attr_set{false};
+    if (!attr_set.load(std::memory_order_acquire)) {
+        hipError_t e = hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)shm);
+        if (e != hipSuccess) return e;
+        attr_set.store(true, std::memory_order_release);
+    }
+    KERN<<<grid, threads, shm, st>>>(t);
+    return hipGetLastError();
+}
+
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, bool GATHER,
           bool OB = false>
 hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
@@ -576,22 +593,17 @@ hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     constexpr int WPF = GATHER ? QLIN_GATHER_WPF : (B4 <= 8 ? QLIN_PREFILL_WPF : 2);
     const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
     static_assert(3 * BM * BK * 2 + 2 * BN * LROW <= 160 * 1024, "LDS budget");
-    auto run = [&](auto kern) -> hipError_t {
-        static bool attr_set = false;  // per instantiation, host side
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute(
-                (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
-        kern<<<grid, WM * WN * 64, shm, st>>>(t);
-        return hipGetLastError();
-    };
+    constexpr int NTH = WM * WN * 64;
     // the code prefetch depth must divide the number of 64-wide steps
     const int nk = t.K / BK;
-    if (nk % WPF == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, WPF, OB>);
-    if (nk % 2 == 0) return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 2, OB>);
-    return run(qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 1, OB>);
+    if (nk % WPF == 0)
+        return launch_with_lds<qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, WPF, OB>>(
+            t, grid, NTH, shm, st);
+    if (nk % 2 == 0)
+        return launch_with_lds<qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 2, OB>>(
+            t, grid, NTH, shm, st);
+    return launch_with_lds<qmm_prefill_kernel<MODE, BITS, G, BM, BN, WM, WN, CPC, GATHER, 1, OB>>(
+        t, grid, NTH, shm, st);
 }
 
 // XCD grid for the plain form: the 8 XCDs take an xgm x (8/xgm) grid of

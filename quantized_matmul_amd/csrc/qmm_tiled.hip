@@ -24,6 +24,8 @@
 
 #include "qlin_common.h"
 
+#include <atomic>
+
 namespace qlin {
 namespace {
 
@@ -454,12 +456,14 @@ template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, bool GATHER
 hipError_t launch_cfg(const TiledArgs& t, int grid, hipStream_t st) {
     const size_t shm = (size_t)2 * (BM + BN) * LROW;
     auto kern = qmm_tiled_kernel<MODE, BITS, G, BM, BN, WM, WN, GATHER>;
-    static bool attr_set = false;  // per instantiation, host side
-    if (!attr_set) {
+    // one kernel per instantiation: the attribute is set once (an atomic
+    // flag, so concurrent callers at worst set it twice)
+    static std::atomic<bool> attr_set{false};
+    if (!attr_set.load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set.store(true, std::memory_order_release);
     }
     kern<<<grid, NTHREADS, shm, st>>>(t);
     return hipGetLastError();
