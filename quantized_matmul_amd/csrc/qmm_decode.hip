@@ -272,7 +272,7 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER, int CB>
 __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
-    static_assert(CB == 1 || (CB == 2 && DX && !F::AFF && !GATHER), "two column blocks: direct-x path");
+    static_assert(CB == 1 || (CB == 2 && !GATHER), "two column blocks: plain forms");
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
     static_assert(!GATHER || !DX, "the gather form stages x in LDS");
@@ -408,7 +408,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
     // that staging x waits only for x (loads complete in order)
     constexpr int SB = F::AFF ? UPW * F::GPU * 2 : UPW * F::GPU;  // bytes per slice
     constexpr int SW = (SB + 3) / 4;
-    uint32_t sraw[CB][SW], zraw[F::AFF ? SW : 1];
+    uint32_t sraw[CB][SW], zraw[CB][F::AFF ? SW : 1];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         constexpr uint32_t SBYTES = F::AFF ? 2u : 1u;
@@ -428,7 +428,8 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
                 sraw[cb][4 * v + 2] = t[2]; sraw[cb][4 * v + 3] = t[3];
                 if constexpr (F::AFF) {
                     const u32x4 tz = __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)soff, 16 * v, 0);
-                    zraw[4 * v] = tz[0]; zraw[4 * v + 1] = tz[1]; zraw[4 * v + 2] = tz[2]; zraw[4 * v + 3] = tz[3];
+                    zraw[cb][4 * v] = tz[0]; zraw[cb][4 * v + 1] = tz[1];
+                    zraw[cb][4 * v + 2] = tz[2]; zraw[cb][4 * v + 3] = tz[3];
                 }
             }
         } else if constexpr (SB == 8) {
@@ -436,14 +437,14 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
             sraw[cb][0] = t[0]; sraw[cb][1] = t[1];
             if constexpr (F::AFF) {
                 const u32x2 tz = __builtin_amdgcn_raw_buffer_load_b64(zrs, (int)soff, 0, 0);
-                zraw[0] = tz[0]; zraw[1] = tz[1];
+                zraw[cb][0] = tz[0]; zraw[cb][1] = tz[1];
             }
         } else if constexpr (SB == 4) {
             sraw[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)soff, 0, 0);
-            if constexpr (F::AFF) zraw[0] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)soff, 0, 0);
+            if constexpr (F::AFF) zraw[cb][0] = __builtin_amdgcn_raw_buffer_load_b32(zrs, (int)soff, 0, 0);
         } else {
             sraw[cb][0] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)soff, 0, 0);
-            if constexpr (F::AFF) zraw[0] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)soff, 0, 0);
+            if constexpr (F::AFF) zraw[cb][0] = __builtin_amdgcn_raw_buffer_load_b16(zrs, (int)soff, 0, 0);
         }
     }
 
@@ -633,16 +634,19 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
                         const int wi = ls / F::WS;
                         const int gw = uu * F::GPU + (F::S == 2 ? 2 * wi : wi);
                         const int sh = (F::S == 2) ? 16 * (j >> 1) : 16 * (gw & 1);
-                        const float s = bf16_bits_to_f32((sraw[0][gw >> 1] >> sh) & 0xFFFFu);
-                        const float z = bf16_bits_to_f32((zraw[gw >> 1] >> sh) & 0xFFFFu);
-                        const float zz = __builtin_fmaf(-F::OFF, s, z);
 #pragma unroll
-                        for (int rr = 0; rr < MREG; ++rr) {
-                            float xs;
-                            if constexpr (XS) xs = xgroup_sum(rr, gw);
-                            else xs = dsum[rr];
-                            ysum[0][rr] = __builtin_fmaf(s, acc[0][rr], ysum[0][rr]);
-                            ysum[0][rr] = __builtin_fmaf(zz, xs, ysum[0][rr]);
+                        for (int b = 0; b < CB; ++b) {
+                            const float s = bf16_bits_to_f32((sraw[b][gw >> 1] >> sh) & 0xFFFFu);
+                            const float z = bf16_bits_to_f32((zraw[b][gw >> 1] >> sh) & 0xFFFFu);
+                            const float zz = __builtin_fmaf(-F::OFF, s, z);
+#pragma unroll
+                            for (int rr = 0; rr < MREG; ++rr) {
+                                float xs;
+                                if constexpr (XS) xs = xgroup_sum(rr, gw);
+                                else xs = dsum[rr];
+                                ysum[b][rr] = __builtin_fmaf(s, acc[b][rr], ysum[b][rr]);
+                                ysum[b][rr] = __builtin_fmaf(zz, xs, ysum[b][rr]);
+                            }
                         }
                     }
                 }
@@ -760,8 +764,15 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, h
     // group sums of x instead of the all-ones MFMA: affine, one row slot, M <= 4
     constexpr bool XSOK = Fmt<MODE, BITS, G>::AFF && Fmt<MODE, BITS, G>::S == 1 && !DX;
     if constexpr (CB == 2) {
-        // direct x, microscaled: rows past 4 in registers (MREG 4)
-        return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, true, false, false, 2>);
+        if constexpr (DX) {
+            // direct x, microscaled: rows past 4 in registers (MREG 4)
+            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, true, false, false, 2>);
+        } else {
+            // staged x shared by the wave's two column blocks (M >= 2)
+            if (mreg <= 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, false, XSOK, false, 2>);
+            if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, XSOK, false, 2>);
+            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, false, 2>);
+        }
     } else {
         if constexpr (!DX) {
             if (gather_tiles > 0) {   // a tile holds 1 .. a.M rows
@@ -835,20 +846,28 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
 #ifndef QLIN_DECODE_DX_CB
 #define QLIN_DECODE_DX_CB 2
 #endif
-    if constexpr (DX && QLIN_DECODE_DX_CB == 2) {
-        // two column blocks per wave (at most 8 waves: longer slices)
+#ifndef QLIN_DECODE_STAGED_CB2_MIN_M
+#define QLIN_DECODE_STAGED_CB2_MIN_M 2
+#endif
+    // two column blocks per wave (at most 8 waves: longer slices): direct x
+    // fragments always; staged x from QLIN_DECODE_STAGED_CB2_MIN_M rows up,
+    // where every workgroup re-reading all of x from L2 rivals the weight
+    // stream (M8: 64 KB of x per workgroup against 56 KB of weights)
+    if ((DX && QLIN_DECODE_DX_CB == 2) || (!DX && gather_tiles == 0 && a.M >= QLIN_DECODE_STAGED_CB2_MIN_M)) {
         int upw2 = upw;
         while (upw2 < 16 && nunits / upw2 > 8) upw2 <<= 1;
-        if (nunits % upw2 == 0 && nunits / upw2 <= 8) {
+        // staged x: a wave's slice of every row fits its chunk registers
+        const bool fits = DX || (int64_t)a.M * upw2 * F::U <= 4096;
+        if (fits && nunits % upw2 == 0 && nunits / upw2 <= 8) {
             DecodeArgs a2 = a;
             a2.cols = decode_columns((a.N + 1) / 2);
             const int ks2 = nunits / upw2;
             switch (upw2) {
-            case 16: return launch_upw<MODE, BITS, G, 16, true, 2>(a2, ks2, mreg, 0, st);
-            case 8: return launch_upw<MODE, BITS, G, 8, true, 2>(a2, ks2, mreg, 0, st);
-            case 4: return launch_upw<MODE, BITS, G, 4, true, 2>(a2, ks2, mreg, 0, st);
-            case 2: return launch_upw<MODE, BITS, G, 2, true, 2>(a2, ks2, mreg, 0, st);
-            default: return launch_upw<MODE, BITS, G, 1, true, 2>(a2, ks2, mreg, 0, st);
+            case 16: return launch_upw<MODE, BITS, G, 16, DX, 2>(a2, ks2, mreg, 0, st);
+            case 8: return launch_upw<MODE, BITS, G, 8, DX, 2>(a2, ks2, mreg, 0, st);
+            case 4: return launch_upw<MODE, BITS, G, 4, DX, 2>(a2, ks2, mreg, 0, st);
+            case 2: return launch_upw<MODE, BITS, G, 2, DX, 2>(a2, ks2, mreg, 0, st);
+            default: return launch_upw<MODE, BITS, G, 1, DX, 2>(a2, ks2, mreg, 0, st);
             }
         }
     }
