@@ -53,8 +53,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                          "(the sharded form is described in DESIGN.md)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                          "(no multi-GPU form is implemented)"}))
         sys.exit(2)
 
     import torch

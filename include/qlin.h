@@ -60,7 +60,7 @@ typedef enum qlin_dtype {
 typedef enum qlin_status {
     QLIN_OK = 0,
     QLIN_ERR_INVALID_ARGUMENT = 1, /* bad shape, dtype, mode, pairing, pointer */
-    QLIN_ERR_UNSUPPORTED = 2,      /* valid combination this build does not run */
+    QLIN_ERR_UNSUPPORTED = 2,      /* valid combination the library does not run */
     QLIN_ERR_DEVICE = 3            /* a HIP launch or runtime call failed */
 } qlin_status;
 
