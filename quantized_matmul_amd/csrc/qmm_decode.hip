@@ -852,8 +852,11 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     // two column blocks per wave (at most 8 waves: longer slices): direct x
     // fragments always; staged x from QLIN_DECODE_STAGED_CB2_MIN_M rows up,
     // where every workgroup re-reading all of x from L2 rivals the weight
-    // stream (M8: 64 KB of x per workgroup against 56 KB of weights)
-    if ((DX && QLIN_DECODE_DX_CB == 2) || (!DX && gather_tiles == 0 && a.M >= QLIN_DECODE_STAGED_CB2_MIN_M)) {
+    // stream (M8: 64 KB of x per workgroup against 56 KB of weights), and
+    // for 8-bit affine codes at one row too (M1 int8 15.5 -> 13.9 us; 4-bit
+    // and microscaled one-row shapes measured slower this way)
+    const bool staged_cb2 = a.M >= QLIN_DECODE_STAGED_CB2_MIN_M || (F::AFF && BITS == 8);
+    if ((DX && QLIN_DECODE_DX_CB == 2) || (!DX && gather_tiles == 0 && staged_cb2)) {
         int upw2 = upw;
         while (upw2 < 16 && nunits / upw2 > 8) upw2 <<= 1;
         // staged x: a wave's slice of every row fits its chunk registers
