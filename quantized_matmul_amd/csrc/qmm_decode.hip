@@ -272,7 +272,7 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER, int CB>
 __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
-    static_assert(CB == 1 || (CB == 2 && !GATHER), "two column blocks: plain forms");
+    static_assert(CB == 1 || CB == 2, "one or two column blocks per wave");
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
     static_assert(!GATHER || !DX, "the gather form stages x in LDS");
@@ -768,6 +768,11 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, h
             // direct x, microscaled: rows past 4 in registers (MREG 4)
             return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, true, false, false, 2>);
         } else {
+            if (gather_tiles > 0) {   // gather form: both blocks of one row tile
+                if (XSOK && a.M <= 4)
+                    return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, XSOK, true, 2>);
+                return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, true, 2>);
+            }
             // staged x shared by the wave's two column blocks (M >= 2)
             if (mreg <= 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, false, XSOK, false, 2>);
             if (XSOK && a.M <= 4) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, XSOK, false, 2>);
@@ -855,22 +860,33 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     // stream (M8: 64 KB of x per workgroup against 56 KB of weights), and
     // for 8-bit affine codes at one row too (M1 int8 15.5 -> 13.9 us; 4-bit
     // and microscaled one-row shapes measured slower this way)
+#ifndef QLIN_GATHER_CB2
+#define QLIN_GATHER_CB2 1
+#endif
     const bool staged_cb2 = a.M >= QLIN_DECODE_STAGED_CB2_MIN_M || (F::AFF && BITS == 8);
-    if ((DX && QLIN_DECODE_DX_CB == 2) || (!DX && gather_tiles == 0 && staged_cb2)) {
+    // gather form: two blocks per wave share the tile's expert lookup, index
+    // loads and x (2 tokens x top-8 10.1 -> 9.5 us, 8 tokens 27.6 -> 23.7 us,
+    // 16 tokens 37.7 -> 31.5 us) while the grid keeps two workgroups per CU
+    // (1 token: 8 tiles would leave 384 workgroups, 7.2 -> 7.7 us)
+    const bool gather_cb2 = QLIN_GATHER_CB2 && gather_tiles > 0 &&
+                            (int64_t)gather_tiles * ((a.N + 2 * a.cols - 1) / (2 * a.cols)) >=
+                                2 * QLIN_DECODE_CUS;
+    if ((DX && QLIN_DECODE_DX_CB == 2) || (!DX && gather_tiles == 0 && staged_cb2) ||
+        (!DX && gather_cb2)) {
         int upw2 = upw;
         while (upw2 < 16 && nunits / upw2 > 8) upw2 <<= 1;
         // staged x: a wave's slice of every row fits its chunk registers
         const bool fits = DX || (int64_t)a.M * upw2 * F::U <= 4096;
         if (fits && nunits % upw2 == 0 && nunits / upw2 <= 8) {
             DecodeArgs a2 = a;
-            a2.cols = decode_columns((a.N + 1) / 2);
+            if (gather_tiles <= 0) a2.cols = decode_columns((a.N + 1) / 2);
             const int ks2 = nunits / upw2;
             switch (upw2) {
-            case 16: return launch_upw<MODE, BITS, G, 16, DX, 2>(a2, ks2, mreg, 0, st);
-            case 8: return launch_upw<MODE, BITS, G, 8, DX, 2>(a2, ks2, mreg, 0, st);
-            case 4: return launch_upw<MODE, BITS, G, 4, DX, 2>(a2, ks2, mreg, 0, st);
-            case 2: return launch_upw<MODE, BITS, G, 2, DX, 2>(a2, ks2, mreg, 0, st);
-            default: return launch_upw<MODE, BITS, G, 1, DX, 2>(a2, ks2, mreg, 0, st);
+            case 16: return launch_upw<MODE, BITS, G, 16, DX, 2>(a2, ks2, mreg, gather_tiles, st);
+            case 8: return launch_upw<MODE, BITS, G, 8, DX, 2>(a2, ks2, mreg, gather_tiles, st);
+            case 4: return launch_upw<MODE, BITS, G, 4, DX, 2>(a2, ks2, mreg, gather_tiles, st);
+            case 2: return launch_upw<MODE, BITS, G, 2, DX, 2>(a2, ks2, mreg, gather_tiles, st);
+            default: return launch_upw<MODE, BITS, G, 1, DX, 2>(a2, ks2, mreg, gather_tiles, st);
             }
         }
     }

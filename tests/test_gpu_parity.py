@@ -477,6 +477,20 @@ def test_gather_decode_kernel(mode, g, bits):
                     mode=mode, path="decode", wid=73)
 
 
+@pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 128, 8), ("mxfp4", 32, 4)])
+def test_gather_decode_two_blocks(mode, g, bits):
+    """Gather grids large enough for two column blocks per wave (forced
+    decode path): 12 tokens x top-4 of 16 experts in 16-row tiles, and 8
+    index rows in the one-tile-per-row form; N = 4000 leaves the last block
+    pair ragged."""
+    K, N, E = 1024, 4000, 16
+    rhs = synth.topk_distinct(12, E, 4, 76)
+    lhs = np.repeat(np.arange(12, dtype=np.uint32), 4).reshape(12, 4)
+    run_gather_case(12, 1, K, N, E, rhs, lhs, bits=bits, g=g, mode=mode, path="decode", wid=76)
+    run_gather_case(8, 1, K, N, E, [3, 9, 3, 14, 0, 7, 11, 2], None, bits=bits, g=g, mode=mode,
+                    path="decode", wid=77)
+
+
 def test_gather_sorted_flag_is_only_a_hint():
     """Flag set on indices that are not sorted: results must not change."""
     run_gather_case(6, 1, 256, 64, 4, [3, 0, 1, 3, 2, 0], None, sorted_indices=True, wid=67)
