@@ -358,14 +358,20 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
 #define QLIN_BUCKET_THREADS 512   // 8 waves: MoE 4096 rows ~1.8 us faster than 4
 #endif
 constexpr int BUCKET_THREADS = QLIN_BUCKET_THREADS;
-constexpr int BCACHE = 4096 / BUCKET_THREADS;
+// a single wave for few index rows (decode-sized batches): its barriers cost
+// nothing and the one workgroup is all there is to launch
+#ifndef QLIN_BUCKET_SMALL_R
+#define QLIN_BUCKET_SMALL_R 512
+#endif
 
-__global__ void __launch_bounds__(BUCKET_THREADS) bucket_kernel(const uint32_t* __restrict__ rhs, int R,
+template <int NTH>
+__global__ void __launch_bounds__(NTH) bucket_kernel(const uint32_t* __restrict__ rhs, int R,
                                                                 int E, int M, int BMrows, int sorted,
                                                                 uint32_t* __restrict__ offsets,
                                                                 uint32_t* __restrict__ tiles,
                                                                 uint32_t* __restrict__ perm) {
-    constexpr int NT = BUCKET_THREADS;
+    constexpr int NT = NTH;
+    constexpr int BCACHE = NT >= 512 ? 4096 / NT : 8;   // rows per thread kept in registers
     extern __shared__ uint32_t sh[];
     uint32_t* cnt = sh;          // [E]
     uint32_t* cur = sh + E;      // [E]
@@ -525,8 +531,13 @@ hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, i
     const size_t shm = (size_t)2 * E * sizeof(uint32_t);
     if (shm > 64 * 1024) return hipErrorInvalidValue;
     if (rows_per_tile < 1) return hipErrorInvalidValue;
-    bucket_kernel<<<1, BUCKET_THREADS, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted,
-                                                  *offsets, *offsets + (E + 1), *perm);
+    if (R <= QLIN_BUCKET_SMALL_R)
+        bucket_kernel<64><<<1, 64, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted,
+                                              *offsets, *offsets + (E + 1), *perm);
+    else
+        bucket_kernel<BUCKET_THREADS><<<1, BUCKET_THREADS, shm, st>>>(rhs, (int)R, (int)E, (int)M,
+                                                                      rows_per_tile, sorted, *offsets,
+                                                                      *offsets + (E + 1), *perm);
     return hipGetLastError();
 }
 
