@@ -8,11 +8,13 @@
 // W, so each lane owns packed words of one column range and walks K:
 //   * per row k the group scale is folded into x (a = x[m,k] * s, one multiply
 //     per row and group) and the bias term x[m,k] * z is summed once per row;
-//   * codes become fp32 and accumulate with one FMA each (fp32 throughout);
-//   * a wave load covers 8 rows x 8 packed words, so a workgroup spans few
-//     columns and the grid has enough workgroups; its 16 waves split K and
-//     meet once in LDS; the weight words stream through a 16-deep prefetch
-//     ring;
+//   * codes become fp32 and accumulate with one FMA each (fp32 throughout;
+//     E2M1 / E4M3 codes by the gfx950 converts, two per instruction);
+//   * a wave load covers 8 rows x 8 packed words (one activation row of
+//     microscaled or 2-bit codes: 32 or 16 rows, each lane a 16- or 8-byte
+//     piece of one group), so a workgroup spans few columns and the grid has
+//     enough workgroups; its 16 waves split K and meet once in LDS; the
+//     weight words stream through a prefetch ring;
 //   * x for all of K is staged in LDS up front; each row's scale and bias
 //     ride in the prefetch ring with its packed word (staging them up front
 //     serialised thousands of scattered 2-byte loads before the weight
@@ -24,6 +26,7 @@ namespace qlin {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 struct NtArgs {
     const uint16_t* x;   // bf16 [M, K]
@@ -35,28 +38,34 @@ struct NtArgs {
     OutBias ob;          // dense-layer bias
 };
 
-// Lane (rr, cl) = (lane / WPB, lane % WPB) handles packed word c0 + cl of
-// row k = RPS * step + rr: one wave load covers RPS = 64 / WPB rows x WPB
-// words. The NW waves of a workgroup split K. Each lane keeps RING2 steps
-// (word, scale, bias) in flight: 16 for up to 2 activation rows of affine
-// codes (32 for one row), fewer otherwise (the accumulators and decoding
-// take the registers). MR = activation rows rounded up (<= 8).
-template <int MODE, int BITS, int G, int MR, int WPB, int NW>
+// Lane (rr, cl) = (lane / LPR, lane % LPR) handles the VW packed words
+// c0 + VW*cl .. c0 + VW*cl + VW-1 of row k = RPS * step + rr: one wave load
+// covers RPS = 64 / LPR rows x WPB words (LPR = WPB / VW lanes per row). The
+// VW words of a lane lie in one quantization group. The NW waves of a
+// workgroup split K. Each lane keeps RING2 steps (words, scale, bias) in
+// flight. MR = activation rows rounded up (<= 8).
+template <int MODE, int BITS, int G, int MR, int WPB, int NW, int VW>
 __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
+    constexpr int PER = 32 / BITS;
+    static_assert(VW == 1 || VW == 2 || VW == 4, "words per lane");
+    static_assert((G / PER) % VW == 0 && WPB % VW == 0, "a lane's words share one group");
     // steps in flight per lane (microscaled decoding needs more registers):
-    // the kernel is bound by the bytes each lane keeps in flight, so one
-    // activation row of 4- or 8-bit affine codes takes 32 (126 registers, no
-    // spills; 25 -> 22.8 us at M1), two rows 16
-    constexpr int RING2 = (MR == 1 && MODE == AFFINE && BITS >= 4) ? 32
+    // the kernel is bound by the bytes each lane keeps in flight. With one
+    // word per lane, one activation row of 4- or 8-bit affine codes takes 32
+    // (126 registers, no spills; 25 -> 22.8 us at M1), two rows 16. With
+    // 16-byte lanes a step already carries four words.
+    constexpr int RING2 = VW > 1 ? 8
+                        : (MR == 1 && MODE == AFFINE && BITS >= 4) ? 32
                         : (MR <= 2 && MODE == AFFINE) ? 16 : (MR <= 4 ? 8 : 4);
     constexpr int NWAVES = NW;
-    constexpr int RPS = 64 / WPB;                     // rows per step
-    constexpr int PER = 32 / BITS;
+    constexpr int LPR = WPB / VW;                     // lanes per row
+    constexpr int RPS = 64 / LPR;                     // rows per step
+    constexpr int CPL = VW * PER;                     // columns per lane
     constexpr bool AFF = MODE == AFFINE;
     constexpr int SBYTES = AFF ? 2 : 1;               // bytes per scale value
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int rr = lane / WPB, cl = lane % WPB;
+    const int rr = lane / LPR, cl = lane % LPR;
     const int K = a.K, N = a.N;
     const int wcols = N / PER;                        // packed words per W row
     // Workgroups are dealt to the 8 XCDs round-robin. Neighbouring column
@@ -66,7 +75,7 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     // fetched once per XCD.
     int cb = blockIdx.x;
     if ((gridDim.x & 7) == 0) cb = (cb & 7) * (gridDim.x >> 3) + (cb >> 3);
-    const int c = cb * WPB + cl;                      // word column of the lane
+    const int c = cb * WPB + cl * VW;                 // first word column of the lane
     const bool active = c < wcols;
     const int gpr = N / G;                            // groups per W row
     const int g0 = (cb * WPB * PER) / G;              // first group of the workgroup
@@ -104,16 +113,16 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     const int T = ((steps_total + NWAVES - 1) / NWAVES + RING2 - 1) / RING2 * RING2;
     const int s0 = wv * T;
 
-    float acc[MR][PER], zacc[MR];
+    float acc[MR][CPL], zacc[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         zacc[m] = 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[m][e] = 0.f;
+        for (int e = 0; e < CPL; ++e) acc[m][e] = 0.f;
     }
 
     const uint32_t* wp = a.wq + (active ? c : 0);
-    uint32_t rw[RING2], rs[RING2], rz[RING2];
+    uint32_t rw[RING2][VW], rs[RING2], rz[RING2];
     const uint32_t sbytes_all = (uint32_t)K * (uint32_t)gpr * SBYTES;
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.scales), (short)0, (int)sbytes_all, 0x00020000);
@@ -124,7 +133,16 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     auto fetch = [&](int slot, int st) {
         const int k = RPS * st + rr;
         const int kk = (active && k < K) ? k : 0;
-        rw[slot] = wp[(size_t)kk * wcols];
+        const uint32_t* src = wp + (size_t)kk * wcols;
+        if constexpr (VW == 4) {
+            const u32x4 v = *(const u32x4*)src;
+            rw[slot][0] = v.x; rw[slot][1] = v.y; rw[slot][2] = v.z; rw[slot][3] = v.w;
+        } else if constexpr (VW == 2) {
+            const u32x2 v = *(const u32x2*)src;
+            rw[slot][0] = v.x; rw[slot][1] = v.y;
+        } else {
+            rw[slot][0] = *src;
+        }
         const uint32_t so = ((uint32_t)kk * (uint32_t)gpr + gcol) * (uint32_t)SBYTES;
         if constexpr (AFF) {
             rs[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, (int)so, 0, 0);
@@ -134,7 +152,6 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
         }
     };
     auto consume = [&](int slot, int st) {
-        const uint32_t w = rw[slot];
         const int kr = RPS * st + rr;
         const bool ok = active && kr < K;
         const int k = ok ? kr : 0;
@@ -148,38 +165,55 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
         }
         s = ok ? s : 0.f;
         z = ok ? z : 0.f;
-        float f[PER];
-        if constexpr (AFF && BITS == 4) {
-            const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                f[2 * q] = (float)((lo >> (8 * q)) & 0xFFu);
-                f[2 * q + 1] = (float)((hi >> (8 * q)) & 0xFFu);
-            }
-        } else if constexpr (AFF && BITS == 8) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) f[q] = (float)((w >> (8 * q)) & 0xFFu);
-        } else if constexpr (AFF) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t mm = (w >> (2 * t)) & 0x03030303u;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) f[4 * q + t] = (float)((mm >> (8 * q)) & 0xFFu);
-            }
-        } else if constexpr (MODE == MXFP8) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) f[q] = e4m3_to_f32((w >> (8 * q)) & 0xFFu);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((w >> (4 * e)) & 0xFu);
-        }
+        float av[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             const float xv = bf16_bits_to_f32(xs[m * K + k]);
-            const float av = xv * s;
+            av[m] = xv * s;
             if constexpr (AFF) zacc[m] = __builtin_fmaf(xv, z, zacc[m]);
+        }
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[m][e] = __builtin_fmaf(av, f[e], acc[m][e]);
+        for (int j = 0; j < VW; ++j) {
+            const uint32_t w = rw[slot][j];
+            float f[PER];
+            if constexpr (AFF && BITS == 4) {
+                const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f[2 * q] = (float)((lo >> (8 * q)) & 0xFFu);
+                    f[2 * q + 1] = (float)((hi >> (8 * q)) & 0xFFu);
+                }
+            } else if constexpr (AFF && BITS == 8) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) f[q] = (float)((w >> (8 * q)) & 0xFFu);
+            } else if constexpr (AFF) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t mm = (w >> (2 * t)) & 0x03030303u;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) f[4 * q + t] = (float)((mm >> (8 * q)) & 0xFFu);
+                }
+            } else if constexpr (MODE == MXFP8) {
+                // gfx950 converts two E4M3 codes per instruction (unit scale:
+                // the group scale is already in av)
+                const auto lo2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+                const auto hi2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+                f[0] = lo2[0]; f[1] = lo2[1]; f[2] = hi2[0]; f[3] = hi2[1];
+            } else {
+                // two E2M1 codes per instruction, byte q = codes 2q (low
+                // nibble) and 2q + 1
+                const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+                const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+                const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+                const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+                f[0] = p0[0]; f[1] = p0[1]; f[2] = p1[0]; f[3] = p1[1];
+                f[4] = p2[0]; f[5] = p2[1]; f[6] = p3[0]; f[7] = p3[1];
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int e = 0; e < PER; ++e)
+                    acc[m][j * PER + e] = __builtin_fmaf(av[m], f[e], acc[m][j * PER + e]);
         }
     };
 #pragma unroll
@@ -198,10 +232,10 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
+        for (int e = 0; e < CPL; ++e) {
             float v = acc[m][e] + zacc[m];
 #pragma unroll
-            for (int off = WPB; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+            for (int off = LPR; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
             acc[m][e] = v;
         }
     __syncthreads();
@@ -213,7 +247,7 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
         if (m >= a.M) break;
         if (rr == 0) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) red[(wv * WPB + cl) * PER + e] = acc[m][e];
+            for (int e = 0; e < CPL; ++e) red[(wv * WPB + cl * VW) * PER + e] = acc[m][e];
         }
         __syncthreads();
         for (int o = tid; o < WPB * PER; o += 64 * NWAVES) {
@@ -237,6 +271,9 @@ inline int nt_mr(int M) { return M <= 2 ? M : (M <= 4 ? 4 : 8); }
 #endif
 #ifndef QLIN_NT_NW
 #define QLIN_NT_NW 16
+#endif
+#ifndef QLIN_NT_WIDE
+#define QLIN_NT_WIDE 1
 #endif
 
 // waves per workgroup: 16 for up to 4 activation rows, 8 for more (the
@@ -276,11 +313,26 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
         kern<<<blocks, 64 * nw, shm, st>>>(a);
         return hipGetLastError();
     };
+    // One activation row of microscaled or 2-bit codes: each lane loads VW
+    // words (16 or 8 bytes, one group) per row. Measured at M1, N 14336 /
+    // 8192, K 4096 / 8192: mxfp4 35.8 -> 35.2 us, nvfp4 40.5 -> 36.9 us, mxfp8
+    // 38.0 -> 34.4 us, int2 g32 26.2 -> 24.5 us; 4- and 8-bit affine codes and
+    // two or more rows ran slower that way (int4 M1 22.7 -> 25.2 us, M2 27.0
+    // -> 31.3 us) and keep one word per lane.
+    // (at most 32 columns per lane: 2-bit codes take two words)
+    constexpr int VCAP = BITS < 4 ? BITS : 4;
+    constexpr int VWIDE = (G / PER) < VCAP ? (G / PER) : VCAP;
+    constexpr bool WIDE_FMT = VWIDE > 1 && (MODE != AFFINE || BITS == 2);
+    if constexpr (WIDE_FMT) {
+        const bool wide = QLIN_NT_WIDE && a.M == 1 &&
+                          ((uintptr_t)a.wq % (4 * VWIDE)) == 0 && (wcols % VWIDE) == 0;
+        if (wide) return run(qmm_nt_kernel<MODE, BITS, G, 1, WPB, NW, VWIDE>, NW);
+    }
     switch (nt_mr(a.M)) {
-    case 1: return run(qmm_nt_kernel<MODE, BITS, G, 1, WPB, NW>, NW);
-    case 2: return run(qmm_nt_kernel<MODE, BITS, G, 2, WPB, NW>, NW);
-    case 4: return run(qmm_nt_kernel<MODE, BITS, G, 4, WPB, NW>, NW);
-    default: return run(qmm_nt_kernel<MODE, BITS, G, 8, WPB, 8>, 8);
+    case 1: return run(qmm_nt_kernel<MODE, BITS, G, 1, WPB, NW, 1>, NW);
+    case 2: return run(qmm_nt_kernel<MODE, BITS, G, 2, WPB, NW, 1>, NW);
+    case 4: return run(qmm_nt_kernel<MODE, BITS, G, 4, WPB, NW, 1>, NW);
+    default: return run(qmm_nt_kernel<MODE, BITS, G, 8, WPB, 8, 1>, 8);
     }
 }
 

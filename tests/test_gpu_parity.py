@@ -303,6 +303,41 @@ def test_nt_kernel_k_slices(M, N, K, bits, g):
     run_qmm_case(M, N, K, bits, g, "affine", "bf16", False, path="decode", wid=84 + bits)
 
 
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES + [("affine", 32, 2)])
+def test_nt_kernel_wide_lanes_ragged(mode, g, bits):
+    """[in, out] layout, one activation row of microscaled or 2-bit codes
+    (each lane loads several words of one group): the last column block is
+    part-filled (672 columns) and K is ragged against the waves' slices."""
+    run_qmm_case(1, 672, 1000, bits, g, mode, "bf16", False, path="decode", wid=88)
+
+
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES + [("affine", 32, 2)])
+def test_nt_kernel_unaligned_weight_pointer(mode, g, bits):
+    """Packed words that start 4 bytes past a 16-byte boundary take the
+    one-word-per-lane form and give the same values."""
+    N, K = 768, 512
+    w, wb = gpu_weight((K, N), 0.02, 89, "bf16")
+    xt, xb = synth.normal((1, K), 1.0, 89, synth.ACT, "bf16")
+    qw, (wq, sc, bi) = quantize_both(w, wb, "bf16", g, bits, mode, False)
+    flat = torch.empty(qw.value.numel() + 1, dtype=qw.value.dtype, device=DEV)
+    shifted = flat[1:].view(qw.value.shape)
+    shifted.copy_(qw.value)
+    assert shifted.data_ptr() % 16 == 4
+    qs = qm.QuantizedWeight(shifted, qw.scales, qw.biases, qw.group_size, qw.bits, qw.transpose, qw.mode)
+    x = xt.to(DEV)
+    os.environ["QLIN_FORCE_PATH"] = "decode"
+    try:
+        y = qm.quantized_matmul(x, qs)
+        y0 = qm.quantized_matmul(x, qw)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("QLIN_FORCE_PATH", None)
+    yref = oracle.quantized_matmul(xb, "bf16", wq, sc, bi, False, g, bits, mode,
+                                   scale_dtype=("bf16" if mode == "affine" else "u8"))
+    assert normwise_rel_err(y, yref) <= tolerance(torch.bfloat16, K)
+    assert normwise_rel_err(y0, yref) <= tolerance(torch.bfloat16, K)
+
+
 def test_nt_kernel_repeat_is_deterministic():
     """Partial sums meet in a fixed order: repeated calls agree bit for bit."""
     w, _ = gpu_weight((4096, 2048), 0.02, 86, "bf16")
