@@ -125,6 +125,37 @@ qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, 
                                   void* stream);
 
 /*
+ * qlin_quantized_matmul_workspace_bytes -- device workspace that lets
+ * qlin_quantized_matmul_ws split K over workgroups for this shape: the
+ * [in, out] layout (transpose == 0) with 1..4 rows of bf16 x (1..2 for
+ * 2-bit codes) and K longer than one slice. 0 when the shape takes no
+ * workspace (then qlin_quantized_matmul_ws is qlin_quantized_matmul). The
+ * size assumes a 16-byte aligned wq; with another wq the call also falls
+ * back to qlin_quantized_matmul.
+ */
+size_t qlin_quantized_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int transpose,
+                                             int group_size, int bits, const char* mode);
+
+/*
+ * qlin_quantized_matmul_ws -- qlin_quantized_matmul with a caller's
+ * workspace ("EMLX.Quantization" quantized_matmul, the same operation).
+ * With at least qlin_quantized_matmul_workspace_bytes(...) bytes the
+ * [in, out] layout at few rows splits K over workgroups: each stores fp32
+ * partial sums of its slice of K in the workspace and a second kernel adds
+ * the slices in a fixed order (results do not depend on scheduling). With
+ * workspace NULL, a smaller workspace or any other shape the call is
+ * qlin_quantized_matmul's. The workspace is device memory the caller owns,
+ * 16-byte aligned, overwritten; calls that share one workspace must not
+ * overlap. Arguments and errors as for qlin_quantized_matmul, plus
+ * QLIN_ERR_INVALID_ARGUMENT for a misaligned workspace.
+ */
+qlin_status qlin_quantized_matmul_ws(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                     const uint32_t* wq, const void* scales, const void* biases,
+                                     qlin_dtype scale_dtype, int64_t N, int transpose,
+                                     int group_size, int bits, const char* mode, void* workspace,
+                                     size_t workspace_bytes, void* y, void* stream);
+
+/*
  * qlin_quantized_dense -- the dense layer on a quantized weight: y = x . W^T
  * (or x . W) plus a bias, fused into the matmul's output stage
  * ("Emily.Quantization.Layers" quantized_dense: x @ W (+ bias), the bias a

@@ -25,5 +25,6 @@ from ._binding import (  # noqa: F401
     qqmm_workspace_bytes,
     quantized_dense,
     quantized_matmul,
+    quantized_matmul_workspace_bytes,
     MODE_DEFAULTS,
 )

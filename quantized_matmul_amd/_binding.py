@@ -54,6 +54,11 @@ def load_library():
                                          cs, vp, i32, ctypes.c_double, vp, vp]
     lib.qlin_gather_qmm.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, vp, vp,
                                     i64, i32, i32, i32, cs, i32, vp, sz, vp, vp]
+    lib.qlin_quantized_matmul_ws.argtypes = [vp, i32, i64, i64, vp, vp, vp, i32, i64, i32, i32,
+                                             i32, cs, vp, sz, vp, vp]
+    lib.qlin_quantized_matmul_ws.restype = i32
+    lib.qlin_quantized_matmul_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, cs]
+    lib.qlin_quantized_matmul_workspace_bytes.restype = sz
     lib.qlin_qqmm.argtypes = [vp, i32, i64, i64, vp, vp, i64, i32, i32, i32, cs, vp, sz, vp, vp]
     lib.qlin_qqmm.restype = i32
     lib.qlin_qqmm_workspace_bytes.argtypes = [i64, i64]
@@ -161,12 +166,23 @@ def _out(out, shape, dtype, dev):
     return out
 
 
+def quantized_matmul_workspace_bytes(M: int, K: int, N: int, transpose: bool, group_size: int,
+                                     bits: int, mode: str = "affine") -> int:
+    """qlin_quantized_matmul_workspace_bytes (0: the shape takes none)."""
+    return int(load_library().qlin_quantized_matmul_workspace_bytes(
+        M, K, N, int(transpose), group_size, bits, mode.encode()))
+
+
 def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """qlin_quantized_matmul: x [..., K] -> y [..., N] in x's dtype.
 
     W is 2-D: [N, K] packed along K when qw.transpose, else [K, N] packed
-    along N ("Emily.Quantization.Layers", quantized_dense).
+    along N ("Emily.Quantization.Layers", quantized_dense). Shapes that take
+    a workspace (the [in, out] layout at few bf16 rows, where K is split over
+    workgroups) get one from torch's allocator unless `workspace` (a uint8
+    device tensor) is given; the call then goes to qlin_quantized_matmul_ws.
     """
     lib = load_library()
     dev = _dev(x)
@@ -182,10 +198,25 @@ def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
         raise ValueError(f"x's last dim {x.shape[-1]} does not match the weight's K={K}")
     M = x.numel() // K if K else 0
     y = _out(out, tuple(x.shape[:-1]) + (N,), x.dtype, dev)
-    rc = lib.qlin_quantized_matmul(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value),
-                                   _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype], N,
-                                   int(qw.transpose), qw.group_size, qw.bits, qw.mode.encode(),
-                                   _ptr(y), _stream(dev))
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    elif not qw.transpose and x.dtype == torch.bfloat16 and 1 <= M <= 8:
+        ws_bytes = quantized_matmul_workspace_bytes(M, K, N, False, qw.group_size, qw.bits, qw.mode)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if ws_bytes:
+        rc = lib.qlin_quantized_matmul_ws(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value),
+                                          _ptr(qw.scales), _ptr(qw.biases),
+                                          _DTYPE[qw.scales.dtype], N, int(qw.transpose),
+                                          qw.group_size, qw.bits, qw.mode.encode(),
+                                          _ptr(workspace), ws_bytes, _ptr(y), _stream(dev))
+    else:
+        rc = lib.qlin_quantized_matmul(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value),
+                                       _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype],
+                                       N, int(qw.transpose), qw.group_size, qw.bits,
+                                       qw.mode.encode(), _ptr(y), _stream(dev))
     _check(rc)
     return y
 

@@ -16,6 +16,12 @@
 #include "../../include/qlin.h"
 #include "qlin_common.h"
 
+namespace qlin {
+// [in, out] layout with a caller's workspace (K split over workgroups)
+size_t qmm_nt_split_workspace_bytes(const QmmArgs& q);
+hipError_t launch_qmm_nt_split(const QmmArgs& q, void* workspace, hipStream_t st);
+}  // namespace qlin
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -95,14 +101,22 @@ int forced_path() {
     if (!strcmp(e, "decode")) return 2;
     if (!strcmp(e, "tiled")) return 3;
     if (!strcmp(e, "prefill")) return 4;
+    if (!strcmp(e, "split")) return 5;
     return 0;
 }
 
 qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t* offsets,
-                    hipStream_t st) {
+                    hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0) {
     const int force = forced_path();
     if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_decode_supports(a))
         return device_status(qlin::launch_qmm_decode(a, st), "quantized_matmul (decode kernel)");
+    if (a.R == 0 && ws && (force == 0 || force == 5)) {
+        const size_t need = qlin::qmm_nt_split_workspace_bytes(a);
+        if (need > 0 && ws_bytes >= need)
+            return device_status(qlin::launch_qmm_nt_split(a, ws, st),
+                                 "quantized_matmul ([in,out] K-split kernel)");
+    }
+    if (force == 5) return fail(QLIN_ERR_UNSUPPORTED, "K-split kernel does not take this shape or workspace");
     if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_nt_supports(a))
         return device_status(qlin::launch_qmm_nt(a, st), "quantized_matmul ([in,out] kernel)");
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
@@ -168,7 +182,8 @@ namespace {
 qlin_status qmm_entry(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, const uint32_t* wq,
                       const void* scales, const void* biases, qlin_dtype scale_dtype, int64_t N,
                       int transpose, int group_size, int bits, const char* mode,
-                      const qlin::OutBias& ob, void* y, void* stream) {
+                      const qlin::OutBias& ob, void* y, void* stream, void* ws = nullptr,
+                      size_t ws_bytes = 0) {
     int m;
     if (N <= 0 || K <= 0) return fail(QLIN_ERR_INVALID_ARGUMENT, "N and K must be positive");
     qlin_status st = check_mode(mode, group_size, bits, transpose ? K : N, &m);
@@ -183,6 +198,8 @@ qlin_status qmm_entry(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, c
     if (!x || !wq || !scales || !y) return fail(QLIN_ERR_INVALID_ARGUMENT, "NULL tensor pointer");
     if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31))
         return fail(QLIN_ERR_UNSUPPORTED, "dimensions above 2^31 are not supported");
+    if (ws && ((uintptr_t)ws & 15) != 0)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     qlin::QmmArgs a{};
     a.x = x;
     a.wq = wq;
@@ -199,7 +216,7 @@ qlin_status qmm_entry(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, c
     a.bits = bits;
     a.mode = m;
     a.ob = ob;
-    return run_qmm(a, nullptr, nullptr, (hipStream_t)stream);
+    return run_qmm(a, nullptr, nullptr, (hipStream_t)stream, ws, ws ? ws_bytes : 0);
 }
 
 }  // namespace
@@ -213,6 +230,35 @@ qlin_status qlin_quantized_matmul(const void* x, qlin_dtype x_dtype, int64_t M, 
     const qlin::OutBias none{nullptr, 0.f, qlin::OB_NONE, QLIN_F32};
     return qmm_entry(x, x_dtype, M, K, wq, scales, biases, scale_dtype, N, transpose, group_size,
                      bits, mode, none, y, stream);
+}
+
+size_t qlin_quantized_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, int transpose,
+                                             int group_size, int bits, const char* mode) {
+    int m;
+    if (M < 1 || N <= 0 || K <= 0) return 0;
+    if (check_mode(mode, group_size, bits, transpose ? K : N, &m) != QLIN_OK) return 0;
+    if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31)) return 0;
+    qlin::QmmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.x_dtype = QLIN_BF16;
+    a.scale_dtype = m == qlin::AFFINE ? QLIN_BF16 : QLIN_U8;
+    a.transpose = transpose ? 1 : 0;
+    a.group_size = group_size;
+    a.bits = bits;
+    a.mode = m;
+    return qlin::qmm_nt_split_workspace_bytes(a);
+}
+
+qlin_status qlin_quantized_matmul_ws(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
+                                     const uint32_t* wq, const void* scales, const void* biases,
+                                     qlin_dtype scale_dtype, int64_t N, int transpose,
+                                     int group_size, int bits, const char* mode, void* workspace,
+                                     size_t workspace_bytes, void* y, void* stream) {
+    const qlin::OutBias none{nullptr, 0.f, qlin::OB_NONE, QLIN_F32};
+    return qmm_entry(x, x_dtype, M, K, wq, scales, biases, scale_dtype, N, transpose, group_size,
+                     bits, mode, none, y, stream, workspace, workspace_bytes);
 }
 
 qlin_status qlin_quantized_dense(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,

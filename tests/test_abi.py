@@ -119,6 +119,37 @@ def test_quantized_dense_rejects(lib):
     assert call(x=None, M=0, wq=None, s=None, y=None, bias=FAKE, bdt=BF16) == 0
 
 
+def test_quantized_matmul_ws_sizes_and_rejects(lib):
+    """The workspace query names the [in, out] layout at 1..8 rows only, and
+    the workspace entry point keeps qlin_quantized_matmul's checks."""
+    nb = lib.qlin_quantized_matmul_workspace_bytes
+    need = nb(1, 4096, 14336, 0, 64, 4, b"affine")
+    assert need > 0 and need % (14336 * 4) == 0          # whole fp32 partial rows
+    assert nb(4, 4096, 14336, 0, 64, 4, b"affine") > 0
+    assert nb(8, 4096, 14336, 0, 64, 4, b"affine") == 0  # 5..8 rows: one-pass kernel
+    assert nb(1, 4096, 14336, 1, 64, 4, b"affine") == 0  # [out, in] layout: none
+    assert nb(0, 4096, 14336, 0, 64, 4, b"affine") == 0
+    assert nb(9, 4096, 14336, 0, 64, 4, b"affine") == 0
+    assert nb(4, 4096, 14336, 0, 32, 2, b"affine") == 0  # 2-bit codes: one or two rows
+    assert nb(1, 4096, 14336, 0, 64, 3, b"affine") == 0  # invalid format
+    assert nb(1, 8192, 8192, 0, 32, 4, b"mxfp4") > 0
+    f = lib.qlin_quantized_matmul_ws
+    WS = ctypes.c_void_p(0x2000)
+    base = dict(x=FAKE, xdt=BF16, M=1, K=4096, wq=FAKE, s=FAKE, b=FAKE, sdt=BF16, N=14336, t=0,
+                g=64, bits=4, mode=b"affine", ws=WS, wsb=need, y=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+
+    assert call(ws=ctypes.c_void_p(0x2008)) == INVALID   # 16-byte alignment
+    assert "workspace" in err(lib)
+    assert call(N=100) == INVALID                        # groups run along N
+    assert call(xdt=F32) == INVALID                      # affine: x dtype = scales dtype
+    assert call(x=None) == INVALID
+    assert call(M=0, x=None, ws=None, wsb=0) == 0        # empty: no-op
+
+
 def test_qqmm_rejects(lib):
     q = lib.qlin_qqmm
     need = lib.qlin_qqmm_workspace_bytes(2, 128)

@@ -65,11 +65,16 @@ def test_graph_matmul_paths():
     y4 = torch.empty((4, 1024), dtype=torch.bfloat16, device=DEV)
     yp = torch.empty((300, 512), dtype=torch.bfloat16, device=DEV)
     yd = torch.empty((4, 1024), dtype=torch.bfloat16, device=DEV)
+    yn1 = torch.empty((1, 1024), dtype=torch.bfloat16, device=DEV)
+    # the [in, out] calls take the K-split form with a workspace from torch's
+    # allocator (allocated while capturing, from the graph's pool)
+    assert qm.quantized_matmul_workspace_bytes(4, 2048, 1024, False, 64, 4) > 0
     calls = [lambda: qm.quantized_matmul(x1, qd, out=y1),
              lambda: qm.quantized_matmul(x4, qn, out=y4),
+             lambda: qm.quantized_matmul(x1, qn, out=yn1),
              lambda: qm.quantized_matmul(xp, qx, out=yp),
              lambda: qm.quantized_dense(x4, qd, b, out=yd)]
-    _check_graph(calls, [y1, y4, yp, yd])
+    _check_graph(calls, [y1, y4, yn1, yp, yd])
 
 
 def test_graph_gather_and_qqmm():

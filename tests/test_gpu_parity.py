@@ -338,6 +338,76 @@ def test_nt_kernel_unaligned_weight_pointer(mode, g, bits):
     assert normwise_rel_err(y0, yref) <= tolerance(torch.bfloat16, K)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("bits,g", AFFINE_CASES)
+def test_nt_split_affine(M, bits, g):
+    """[in, out] layout with a workspace: K split over workgroups, partial
+    sums added in a second kernel; ragged last superblock (768 columns)."""
+    N = 8 * 96 if g != 128 else 640
+    if qm.quantized_matmul_workspace_bytes(M, 512, N, False, g, bits) == 0:
+        pytest.skip("no K split at this row count (2-bit codes: 1-2 rows; others 1-4)")
+    run_qmm_case(M, N, 512, bits, g, "affine", "bf16", False, path="split", wid=91 + bits)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
+def test_nt_split_micro(M, mode, g, bits):
+    run_qmm_case(M, 768, 1024, bits, g, mode, "bf16", False, path="split", wid=94)
+
+
+def test_nt_split_row_limits():
+    """The workspace query offers the K split at 1-4 rows (1-2 for 2-bit
+    codes) and not at 5-8, where the one-pass kernel is kept."""
+    q = qm.quantized_matmul_workspace_bytes
+    assert all(q(M, 4096, 14336, False, 64, 4) > 0 for M in (1, 2, 3, 4))
+    assert all(q(M, 4096, 14336, False, 64, 4) == 0 for M in (5, 8))
+    assert q(2, 4096, 14336, False, 32, 2) > 0 and q(3, 4096, 14336, False, 32, 2) == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 4160), (2, 3072, 1000), (3, 640, 2048), (5, 512, 64),
+                                   (8, 1536, 8), (1, 14336, 4096)])
+@pytest.mark.parametrize("bits,g", [(4, 64), (8, 32), (2, 128)])
+def test_nt_split_k_slices(M, N, K, bits, g):
+    """K-split form: ragged last slice, K shorter than one slice, a single
+    row of K, and the decode workload's full shape at one row."""
+    if N % g:
+        pytest.skip("group does not divide N")
+    if qm.quantized_matmul_workspace_bytes(M, K, N, False, g, bits) == 0:
+        pytest.skip("no K split for this shape (one slice, or the row count)")
+    run_qmm_case(M, N, K, bits, g, "affine", "bf16", False, path="split", wid=95 + bits)
+
+
+def test_nt_split_workspace_rules():
+    """A caller's workspace that is too small falls back to the one-pass
+    kernel; repeated calls agree bit for bit; the result matches the
+    one-pass kernel within the matmul bar."""
+    K, N = 2048, 4096
+    w, wb = gpu_weight((K, N), 0.02, 97, "bf16")
+    xt, xb = synth.normal((2, K), 1.0, 97, synth.ACT, "bf16")
+    qw, (wq, sc, bi) = quantize_both(w, wb, "bf16", 64, 4, "affine", False)
+    x = xt.to(DEV)
+    need = qm.quantized_matmul_workspace_bytes(2, K, N, False, 64, 4)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ys = [qm.quantized_matmul(x, qw, workspace=ws) for _ in range(3)]
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    y_small = qm.quantized_matmul(x, qw, workspace=small)
+    os.environ["QLIN_FORCE_PATH"] = "decode"
+    try:
+        y_one = qm.quantized_matmul(x, qw)
+    finally:
+        os.environ.pop("QLIN_FORCE_PATH", None)
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    assert torch.equal(y_small, y_one)                  # fell back to the one-pass kernel
+    yref = oracle.quantized_matmul(xb, "bf16", wq, sc, bi, False, 64, 4, "affine",
+                                   scale_dtype="bf16")
+    tol = tolerance(torch.bfloat16, K)
+    assert normwise_rel_err(ys[0], yref) <= tol
+    assert normwise_rel_err(y_one, yref) <= tol
+
+
 def test_nt_kernel_repeat_is_deterministic():
     """Partial sums meet in a fixed order: repeated calls agree bit for bit."""
     w, _ = gpu_weight((4096, 2048), 0.02, 86, "bf16")
