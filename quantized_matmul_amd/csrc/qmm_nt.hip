@@ -619,6 +619,8 @@ bool qmm_nt_supports(const QmmArgs& q) {
     if (q.M < 1 || q.M > 8) return false;
     if (q.K > (1 << 20) || q.N > (1 << 28)) return false;
     if (q.K % 8 != 0 || ((uintptr_t)q.x & 15) != 0) return false;
+    // scale and bias offsets are 32-bit buffer offsets
+    if (q.K * (q.N / q.group_size) * 2 >= (1LL << 31)) return false;
     return nt_shm((int)q.M, (int)q.K, 32 / q.bits) <= 150 * 1024;
 }
 
