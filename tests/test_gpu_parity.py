@@ -408,6 +408,14 @@ def test_nt_split_workspace_rules():
     assert normwise_rel_err(y_one, yref) <= tol
 
 
+@pytest.mark.parametrize("M", [9, 20, 128])
+@pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("mxfp4", 32, 4)])
+def test_nt_kernel_row_blocks(M, mode, g, bits):
+    """[in, out] layout with 9..128 rows: the few-row kernel over blocks of
+    8 rows (ragged last block)."""
+    run_qmm_case(M, 768, 512, bits, g, mode, "bf16", False, path="decode", wid=98)
+
+
 def test_nt_kernel_repeat_is_deterministic():
     """Partial sums meet in a fixed order: repeated calls agree bit for bit."""
     w, _ = gpu_weight((4096, 2048), 0.02, 86, "bf16")
