@@ -603,3 +603,196 @@ def test_gather_permutation_and_identity():
     y1 = oracle.gather_qmm(x, "bf16", wq, sc, bi, np.full(6, 2), None, True, 64, 4)
     ref = oracle.quantized_matmul(x.reshape(-1, K), "bf16", wq[2], sc[2], bi[2], True, 64, 4)
     assert np.array_equal(y1.reshape(-1, N), ref)
+
+
+# ------------------------------------------------- rounding of the codes
+# The affine code is the nearest-even integer of the IEEE fp32 quotient
+# (w - bias) / scale, and the dequantized value is scale*q + bias with one
+# rounding. These pins take the expected values from numpy's IEEE float32
+# division, numpy's round-half-even rint, and exact fp64 arithmetic: none of
+# them restates the oracle's own code path.
+
+def _ulp_steps(v, k):
+    """v moved k float32 ulps (k may be negative)."""
+    v = np.float32(v)
+    to = np.float32(np.inf if k > 0 else -np.inf)
+    for _ in range(abs(k)):
+        v = np.nextafter(v, to, dtype=np.float32)
+    return v
+
+
+@pytest.mark.parametrize("bits,a,k", [(8, 3, 0), (8, 63, 4), (4, 3, 6), (4, 11, 2), (2, 15, 9), (2, 25, 3)])
+def test_affine_codes_are_ieee_quotient_ties_even(bits, a, k):
+    """Groups with bias 0 and scale s = a*2^-k (the group holds 0 and n*s, so
+    the stored scale is exactly s); the other elements sit on each half-step
+    (m + 1/2)*s and 1-2 ulps around it. Exact half-steps must give the even
+    code (numpy rint); the others must give rint of numpy's IEEE fp32
+    quotient. A reciprocal multiply d*(1/s) or a half-up floor(t + 1/2)
+    changes some of these codes."""
+    n = (1 << bits) - 1
+    g = 64
+    s = np.float32(a * 2.0 ** -k)
+    assert np.float32(np.float32(n * s) / np.float32(n)) == s
+    vals = []
+    for m in range(n):
+        tie = np.float32((m + 0.5) * s)
+        assert np.float64(tie) == (m + 0.5) * np.float64(s)      # exact half-step
+        vals += [tie] + [_ulp_steps(tie, d) for d in (-2, -1, 1, 2)]
+    per = g - 2
+    vals += [vals[-1]] * (-len(vals) % per)
+    rows = np.array(vals, np.float32).reshape(-1, per)
+    w = np.concatenate([np.zeros((len(rows), 1), np.float32),
+                        np.full((len(rows), 1), np.float32(n * s)), rows], axis=1)
+    wq, sc, bi = oracle.quantize(w, "f32", g, bits)
+    assert np.all(sc == s) and np.all(bi == 0)
+    expect = np.clip(np.rint(w / s), 0, n).astype(np.int64)      # IEEE quotient, ties even
+    got = _unpack(wq, bits, g).astype(np.int64)
+    assert np.array_equal(got, expect)
+    # the exact half-steps really are ties and went to the even neighbour
+    ties = (np.float64(w) / np.float64(s)) % 1.0 == 0.5
+    assert ties.sum() >= n and np.all(got[ties] % 2 == 0)
+    # the reciprocal product disagrees with the quotient on some of these
+    # elements, so the test can tell the two apart
+    assert np.any(np.rint(w * np.float32(np.float32(1) / s)) != np.rint(w / s))
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
+def test_affine_dequant_single_rounding(sdt):
+    """dequant = scale*q + bias rounded once to fp32. For the scales and
+    biases drawn here s*q + z is exact in fp64 (s*q has at most 32
+    significant bits and |z| is within 2^12 of |s|), so np.float32 of the fp64
+    value is that one rounding; with fp32 scales, rounding s*q first differs
+    on many elements."""
+    r = np.random.default_rng(21)
+    rows, g, bits = 64, 64, 8
+    G = 4
+    K = G * g
+    s = np.float32(np.abs(r.standard_normal((rows, G))) * 0.01 + 1e-4)
+    z = np.float32(r.standard_normal((rows, G)) * 0.3)
+    if sdt == "bf16":
+        sb, zb = bf16_bits(s), bf16_bits(z)
+        s, z = bf16_to_f32(sb), bf16_to_f32(zb)
+    elif sdt == "f16":
+        sb, zb = s.astype(np.float16).view(np.uint16), z.astype(np.float16).view(np.uint16)
+        s, z = sb.view(np.float16).astype(np.float32), zb.view(np.float16).astype(np.float32)
+    else:
+        sb, zb = s, z
+    q = r.integers(0, 256, size=(rows, K))
+    per = 32 // bits
+    wq = np.zeros((rows, K // per), np.uint32)
+    for j in range(per):
+        wq |= (q[:, j::per].astype(np.uint32) << np.uint32(bits * j))
+    dq = oracle.dequantize(wq, sb, zb, g, bits, scale_dtype=sdt)
+    s64, z64 = s.astype(np.float64).repeat(g, 1), z.astype(np.float64).repeat(g, 1)
+    expect = (s64 * q + z64).astype(np.float32)
+    assert np.array_equal(dq, expect)
+    if sdt == "f32":
+        # with 16-bit scales s*q is exact in fp32 and the two forms agree;
+        # with fp32 scales rounding the product first changes some values
+        two = (s.repeat(g, 1) * q.astype(np.float32)).astype(np.float32) + z.repeat(g, 1)
+        assert np.count_nonzero(two != expect) > 0
+
+
+def test_nvfp4_codes_use_ieee_quotient():
+    """nvfp4 elements are fl32(w / scale) rounded nearest-even into E2M1.
+    Each group holds 6*sc (so the scale byte decodes to exactly sc) and values
+    on and 1-2 ulps around the E2M1 midpoints times sc; expected codes come
+    from numpy's IEEE float32 division and a brute-force nearest-even search.
+    Dividing by way of a reciprocal moves some of them across a midpoint."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    groups, expect_codes, recip_differs = [], [], False
+    for sbyte in range(0x30, 0x48):                  # normal e4m3 scales around 1
+        sc = np.float32(oracle.decode("e4m3", sbyte))
+        vals = []
+        for t in mids:
+            tie = np.float32(t * sc)
+            assert np.float64(tie) == t * np.float64(sc)
+            vals += [tie] + [_ulp_steps(tie, d) for d in (-2, -1, 1, 2)]
+        vals += [-v for v in vals[:10]]
+        for i in range(0, len(vals), 15):
+            chunk = vals[i:i + 15]
+            chunk += [chunk[-1]] * (15 - len(chunk))
+            grp = np.array([6 * sc] + chunk, np.float32)
+            groups.append(grp)
+            q = grp / sc                               # IEEE float32 division
+            expect_codes.append([_e2m1_nearest_even_bruteforce(float(v)) for v in q])
+            rq = grp * np.float32(np.float32(1) / sc)
+            if any(_e2m1_nearest_even_bruteforce(float(v)) != c
+                   for v, c in zip(rq, expect_codes[-1])):
+                recip_differs = True
+    assert recip_differs
+    w = np.stack(groups)
+    wq, sc_b, _ = oracle.quantize(w, "f32", 16, 4, "nvfp4")
+    got = _unpack(wq, 4, 16)
+    assert np.array_equal(got, np.array(expect_codes))
+
+
+@pytest.mark.parametrize("mode,c,xhat", [
+    # mxfp8: amax 1.1 -> shared exponent floor(log2 1.1) - 8 = -8; 1.1*2^8 = 281.6
+    # lies between the E4M3 values 256 and 288 (spacing 32 in [256, 512)) and
+    # is nearer 288, so x-hat = 288 * 2^-8 = 1.125
+    ("mxfp8", 1.1, 1.125),
+    # nvfp4: amax/6 = 0.18333 lies between the E4M3 values 0.171875 and 0.1875
+    # (spacing 2^-6 in [0.125, 0.25)) -> scale 0.1875; 1.1/0.1875 = 5.87 rounds
+    # to the E2M1 value 6 (midpoint 5) -> x-hat = 6 * 0.1875 = 1.125
+    ("nvfp4", 1.1, 1.125),
+    # nvfp4: 0.7/6 = 0.11667 -> E4M3 0.1171875 (spacing 2^-7 in [2^-4, 2^-3));
+    # 0.7/0.1171875 = 5.97 -> 6 -> x-hat = 0.703125
+    ("nvfp4", 0.7, 0.703125),
+    # mxfp8: amax 0.3 -> exponent floor(log2 0.3) - 8 = -10; 0.3*2^10 = 307.2 ->
+    # E4M3 320 (between 288 and 320, nearer 320) -> x-hat = 320 * 2^-10 = 0.3125
+    ("mxfp8", 0.3, 0.3125),
+])
+def test_qqmm_constant_x_closed_form(mode, c, xhat):
+    """x constant off the grid: x-hat is the closed-form value above, and with
+    W on its grid (dequant(W) = W exactly) y = x-hat * (row sums of W),
+    exactly in fp64. Using the unquantized x gives c * (row sums) instead."""
+    g, bits = oracle.MODE_PAIRING[mode]
+    N, K, M = 12, 4 * g, 3
+    W = _micro_grid_x(mode, N, K, seed=95)
+    wq, sc, _ = oracle.quantize(W, "f32", g, bits, mode)
+    assert np.array_equal(oracle.dequantize(wq, sc, None, g, bits, mode), W)
+    x = np.full((M, K), np.float32(c), np.float32)
+    y, xh = oracle.qqmm(x, "f32", wq, sc, True, g, bits, mode, return_xhat=True)
+    assert np.all(xh == np.float32(xhat))
+    rowsum = W.astype(np.float64).sum(1)
+    assert np.array_equal(y, np.broadcast_to(xhat * rowsum, (M, N)))
+    assert not np.allclose(y, np.float64(np.float32(c)) * rowsum, rtol=1e-3, atol=0)
+
+
+@pytest.mark.parametrize("mode", ["nvfp4", "mxfp8"])
+def test_qqmm_differs_from_unquantized_x(mode):
+    """On random x the quantization of x is visible in y: y departs from the
+    product with the unquantized x by more than fp64 rounding could explain
+    (a lower bound beside the error bound above)."""
+    N, K, M = 16, 256, 3
+    tx, _ = synth.normal((M, K), 1.0, 96, synth.ACT, "f32")
+    wq, sc, g, bits = _micro_weight(mode, N, K, 96)
+    y = oracle.qqmm(tx.numpy(), "f32", wq, sc, True, g, bits, mode)
+    y0 = oracle.quantized_matmul(tx.numpy(), "f32", wq, sc, None, True, g, bits, mode)
+    assert np.abs(y - y0).max() > 1e-3 * np.abs(y0).max()
+
+
+def test_affine_scale_rounds_up_in_bf16():
+    """An int8 bf16 group with minimum -0.75 and maximum 255: the fp32 scale
+    is 255.75/255 = 1.00294, which lies below the bf16 midpoint 1.00390625
+    between 1 and 1.0078125. Nearest-even storage would give scale 1 and put
+    the group maximum 0.75 (> scale/2) away from its dequantized value
+    (code 255 -> -0.75 + 255). The stored scale must be the bf16 value just
+    above the fp32 scale (torch nextafter) and keep |w - dq| <= s/2 for every
+    element (the benchmark spec's bound)."""
+    w = np.linspace(-0.75, 255.0, 64, dtype=np.float32)[None, :]
+    wb = bf16_bits(w)
+    wf = bf16_to_f32(wb)
+    assert wf.min() == -0.75 and wf.max() == 255.0
+    wq, sc, bi = oracle.quantize(wb, "bf16", 64, 8)
+    s = float(bf16_to_f32(sc)[0, 0])
+    s32 = np.float32(np.float32(255.75) / np.float32(255))
+    rn = torch.tensor(float(s32)).to(torch.bfloat16)
+    assert float(rn) == 1.0                       # nearest-even would round down
+    up = torch.nextafter(rn, torch.tensor(np.inf, dtype=torch.bfloat16))
+    assert s == float(up) == 1.0078125
+    assert float(bf16_to_f32(bi)[0, 0]) == -0.75
+    dq = oracle.dequantize(wq, sc, bi, 64, 8, scale_dtype="bf16")
+    assert np.all(np.abs(wf - dq) <= s / 2 * (1 + 2 ** -20))
+    assert 255.0 - (-0.75 + 255 * 1.0) > 1.0 / 2   # the bound the down-rounded scale breaks
