@@ -10,14 +10,18 @@ measured in the same run and reported alongside.
 Timing: inputs resident in HBM; decode steps cycle through >= 512 MB of
 distinct weight copies so that the 256 MB Infinity Cache cannot serve them;
 the timed launches are captured in a HIP graph (no host overhead between
-kernels), replayed once untimed, then replayed LOOPS = 5 times, each replay
-of exactly `steps` launches bracketed by torch.cuda.synchronize() and HIP
-events on the launch stream; the median replay is reported. Algorithmic
-bytes = packed W + scales + biases + x + y, each counted once; flops =
-2*M*N*K.
+kernels) and replayed for 200 ms untimed. Each timed replay is bracketed by
+torch.cuda.synchronize() and HIP events on the launch stream, with a short
+spin kernel before the start event so that host launch latency stays
+outside the events. The headline replays exactly `--steps` launches, as
+many times as it takes to cover 2 ms (at least 5); every other workload
+replays >= 2 ms of launches 5 times. The median replay is reported.
+Algorithmic bytes = packed W + scales + biases + x + y, each counted once;
+flops = 2*M*N*K.
 
 cpu_baseline: the CPU oracle (test infrastructure, plain C, fp64) on a
-bounded sample of the same decode workload, timed on this host.
+bounded sample of the same decode workload, timed on this host; the
+prefill block carries its own, on a row sample of the prefill workload.
 """
 import argparse
 import json
@@ -34,7 +38,10 @@ METRIC = "qmm decode GB/s (% of HBM peak) + prefill TFLOP/s; int4 g64 affine"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0}
 ROTATE_BYTES = 512 * 2 ** 20
-LOOPS = 5  # timed loops per workload; the median is reported
+LOOPS = 5          # timed replays per workload (at least); the median is reported
+MAX_LOOPS = 201    # cap on replays of the exact --steps headline graph
+MIN_REPLAY_MS = 2.0  # timed work per workload covers at least this
+WARM_MS = 200.0    # graph replays before timing, per workload
 
 
 def parse():
@@ -85,50 +92,68 @@ def main():
         del w
         return qw
 
-    def timed(fn_list, steps, warmup, graph=True):
-        """Run fn_list[s % len] for `steps` steps; returns seconds per step."""
+    # Host launch latency must not land inside a timed region: before each
+    # timed replay a spin kernel keeps the GPU busy while the host enqueues
+    # the start event and the graph, so the graph's first kernel follows the
+    # event at once.
+    spin_cycles = calibrate_spin(torch, log)
+
+    def timed(fn_list, steps=None, min_ms=MIN_REPLAY_MS):
+        """Time launches of fn_list[s % len] captured in a HIP graph.
+
+        steps given: every timed replay holds exactly that many launches and
+        the replay is repeated until the replays cover min_ms (at least
+        LOOPS times). steps None: a replay holds enough launches (a multiple
+        of len(fn_list)) to last min_ms, replayed LOOPS times. Warm-up: the
+        graph replayed for WARM_MS first. Returns (seconds per launch,
+        launches per replay, timed replays)."""
         stream = torch.cuda.current_stream()
-        for s in range(warmup):
-            fn_list[s % len(fn_list)]()
+        for f in fn_list:
+            f()
         torch.cuda.synchronize()
-        if graph:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for s in range(steps):
-                    fn_list[s % len(fn_list)]()
-            g.replay()  # warm replay
-            torch.cuda.synchronize()
-            # LOOPS timed replays of exactly `steps` launches each; the median
-            # loop is reported (the first loop after a pause runs on cooler
-            # clocks)
-            times = []
-            for _ in range(LOOPS):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1))
-            ms = sorted(times)[len(times) // 2]
-            del g
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 2 * len(fn_list)
+        torch.cuda._sleep(spin_cycles)
+        e0.record(stream)
+        for s in range(reps):
+            fn_list[s % len(fn_list)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        est = e0.elapsed_time(e1) / reps                 # ms per launch, eager
+        if steps is None:
+            n = max(len(fn_list), math.ceil(min_ms / max(est, 1e-4)))
+            n = math.ceil(n / len(fn_list)) * len(fn_list)
+            loops = LOOPS
         else:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for s in range(steps):
+            n = steps
+            loops = min(MAX_LOOPS, max(LOOPS, math.ceil(min_ms / max(est * n, 1e-4))))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(n):
                 fn_list[s % len(fn_list)]()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < WARM_MS / 1e3:
+            g.replay()
+            torch.cuda.synchronize()
+        times = []
+        for _ in range(loops):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(spin_cycles)
+            e0.record(stream)
+            g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-        return ms / 1e3 / steps
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        del g
+        return ms / 1e3 / n, n, loops
 
     # ------------------------------------------------------------ decode
     def bias_vector(N, wid):
         b, _ = synth.normal((N,), 1.0, wid, synth.BIAS, "bf16")
         return b.to(dev)
 
-    def decode_case(M, N, K, bits, g, mode="affine", transpose=True, wid=101, steps=None,
+    def decode_case(M, N, K, bits, g, mode="affine", transpose=True, wid=101, headline=False,
                     dense_bias=False):
         shape = (N, K) if transpose else (K, N)
         qw = make_weight(shape, wid, mode, g, bits, transpose)
@@ -143,9 +168,9 @@ def main():
             fns = [lambda c=c: qm.quantized_dense(x, c, b, out=y) for c in copies]
         else:
             fns = [lambda c=c: qm.quantized_matmul(x, c, out=y) for c in copies]
-        n = steps or args.steps
-        n = max(len(fns), (n // len(fns)) * len(fns))
-        sec = timed(fns, n, args.warmup)
+        # the headline times exactly --steps launches per replay; the other
+        # shapes time replays of >= MIN_REPLAY_MS
+        sec, n, loops = timed(fns, steps=args.steps if headline else None)
         alg = per + x.numel() * 2 + y.numel() * 2 + (N * 2 if dense_bias else 0)
         gbs = alg / sec / 1e9
         del copies, fns
@@ -155,9 +180,9 @@ def main():
                             f"transpose={'true' if transpose else 'false'}",
                 "us": sec * 1e6, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
                 "TFLOP/s": 2 * M * N * K / sec / 1e12, "alg_bytes": alg, "copies": ncopy,
-                "steps": n}
+                "steps": n, "replays": loops}
 
-    def prefill_case(M, N, K, bits, g, mode="affine", wid=201, steps=None, dense_bias=False):
+    def prefill_case(M, N, K, bits, g, mode="affine", wid=201, dense_bias=False):
         qw = make_weight((N, K), wid, mode, g, bits, True)
         x, _ = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
         x = x.to(dev)
@@ -167,15 +192,14 @@ def main():
             fns = [lambda: qm.quantized_dense(x, qw, b, out=y)]
         else:
             fns = [lambda: qm.quantized_matmul(x, qw, out=y)]
-        n = steps or max(10, args.steps // 8)
-        sec = timed(fns, n, min(args.warmup, 5))
+        sec, n, loops = timed(fns)
         flops = 2 * M * N * K
         tf = flops / sec / 1e12
         alg = qw_bytes(qw) + x.numel() * 2 + y.numel() * 2 + (N * 2 if dense_bias else 0)
         op = "quantized_dense (bf16 bias)" if dense_bias else "qmm"
         return {"workload": f"prefill {op} {mode} {bits}-bit g{g} M{M} N{N} K{K} transpose=true",
                 "us": sec * 1e6, "TFLOP/s": tf, "frac_mfma": tf / MFMA_PEAK_TFLOPS["bf16"],
-                "GB/s": alg / sec / 1e9, "flops": flops, "alg_bytes": alg, "steps": n}
+                "GB/s": alg / sec / 1e9, "flops": flops, "alg_bytes": alg, "steps": n, "replays": loops}
 
     def quant_case(N, K, bits, g, mode="affine", wid=401):
         """qlin_quantize of a bf16 W [N, K], then qlin_dequantize back to bf16,
@@ -217,16 +241,15 @@ def main():
                                      mode.encode(), vp(dense[i].data_ptr()), BF16, stream())
             assert rc == 0, rc
 
-        n = max(ncopy, (max(16, args.steps // 8) // ncopy) * ncopy)
-        tq = timed([lambda i=i: q(i) for i in range(ncopy)], n, min(args.warmup, 4))
-        td = timed([lambda i=i: dq(i) for i in range(ncopy)], n, min(args.warmup, 4))
+        tq, n, loops = timed([lambda i=i: q(i) for i in range(ncopy)])
+        td, n, loops = timed([lambda i=i: dq(i) for i in range(ncopy)])
         packed = N * K * bits // 8 + N * G * (4 if mode == "affine" else 1)
         bq = N * K * 2 + packed
         res = []
         for name, t, b in (("quantize", tq, bq), ("dequantize", td, bq)):
             res.append({"workload": f"{name} {mode} {bits}-bit g{g} W bf16 [{N},{K}]",
                         "us": t * 1e6, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / HBM_PEAK_GBS,
-                        "alg_bytes": b, "copies": ncopy, "steps": n})
+                        "alg_bytes": b, "copies": ncopy, "steps": n, "replays": loops})
         del ws, outs, dense
         torch.cuda.empty_cache()
         return res
@@ -244,8 +267,7 @@ def main():
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(qm.qqmm_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
         fns = [lambda c=c: qm.qqmm(x, c, workspace=ws, out=y) for c in copies]
-        n = max(len(fns), (max(16, args.steps // (4 if M <= 16 else 8)) // len(fns)) * len(fns))
-        sec = timed(fns, n, min(args.warmup, 5))
+        sec, n, loops = timed(fns)
         # algorithmic bytes: W, its scales, x read once, y written once
         alg = per + x.numel() * 2 + y.numel() * 2
         flops = 2 * M * N * K
@@ -255,7 +277,7 @@ def main():
                 "us": sec * 1e6, "GB/s": alg / sec / 1e9, "frac_hbm": alg / sec / 1e9 / HBM_PEAK_GBS,
                 "TFLOP/s": flops / sec / 1e12,
                 "frac_mfma": flops / sec / 1e12 / MFMA_PEAK_TFLOPS["bf16"], "alg_bytes": alg,
-                "copies": ncopy, "steps": n}
+                "copies": ncopy, "steps": n, "replays": loops}
 
     def moe_case(sorted_indices, T=512, wid=301):
         """gather_qmm over 64 stacked experts, T tokens x top-8 distinct experts;
@@ -281,8 +303,7 @@ def main():
         y = torch.empty((R, 1, N), dtype=torch.bfloat16, device=dev)
         fns = [lambda c=c: qm.gather_qmm(x, c, rhs_f, lhs_f, sorted_indices=sorted_indices,
                                          workspace=ws, out=y) for c in copies]
-        n = max(len(fns), (max(10, args.steps // 4) // len(fns)) * len(fns))
-        sec = timed(fns, n, min(args.warmup, 5))
+        sec, n, loops = timed(fns)
         # algorithmic bytes: the experts the indices touch, each once
         alg = per * touched // E + x.numel() * 2 + y.numel() * 2 + 2 * R * 4
         flops = 2 * R * N * K
@@ -293,11 +314,11 @@ def main():
                 "us": sec * 1e6, "GB/s": alg / sec / 1e9, "frac_hbm": alg / sec / 1e9 / HBM_PEAK_GBS,
                 "TFLOP/s": flops / sec / 1e12,
                 "frac_mfma": flops / sec / 1e12 / MFMA_PEAK_TFLOPS["bf16"], "alg_bytes": alg,
-                "experts_touched": touched, "copies": ncopy, "steps": n}
+                "experts_touched": touched, "copies": ncopy, "steps": n, "replays": loops}
 
     results = []
     log("decode headline: affine int4 g64 M1 N14336 K4096")
-    head = decode_case(1, 14336, 4096, 4, 64, wid=101)
+    head = decode_case(1, 14336, 4096, 4, 64, wid=101, headline=True)
     results.append(head)
     log(json.dumps(head))
     pre = None
@@ -309,18 +330,15 @@ def main():
     if args.only in ("all", "decode"):
         for (M, bits, g, t) in [(4, 4, 64, True), (8, 4, 64, True), (1, 8, 64, True),
                                 (1, 2, 32, True), (1, 4, 64, False), (4, 4, 64, False)]:
-            r = decode_case(M, 14336, 4096, bits, g, transpose=t, wid=110 + bits,
-                            steps=max(32, args.steps // 4))
+            r = decode_case(M, 14336, 4096, bits, g, transpose=t, wid=110 + bits)
             results.append(r)
             log(json.dumps(r))
         for mode, g, bits in [("mxfp4", 32, 4), ("nvfp4", 16, 4), ("mxfp8", 32, 8)]:
             for M in (1, 16):
-                r = decode_case(M, 8192, 8192, bits, g, mode=mode, wid=120,
-                                steps=max(32, args.steps // 4))
+                r = decode_case(M, 8192, 8192, bits, g, mode=mode, wid=120)
                 results.append(r)
                 log(json.dumps(r))
-        r = decode_case(1, 14336, 4096, 4, 64, wid=101, steps=max(32, args.steps // 4),
-                        dense_bias=True)
+        r = decode_case(1, 14336, 4096, 4, 64, wid=101, dense_bias=True)
         results.append(r)
         log(json.dumps(r))
     if args.only in ("all", "prefill"):
@@ -362,9 +380,11 @@ def main():
         log(f"copy probe: 5 device copies of {n} bytes")
 
     # ------------------------------------------------------------ CPU baseline
-    cpu = None
+    cpu = cpu_pre = None
     if not args.no_cpu:
         cpu = cpu_baseline(args.cpu_seconds, log)
+        if pre is not None:
+            cpu_pre = cpu_baseline_prefill(args.cpu_seconds, log)
 
     # ------------------------------------------------------------ headline
     line = {
@@ -373,6 +393,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": head["steps"],
+        "timed_replays": head["replays"],
         "warmup": args.warmup,
         "ms_per_step": head["us"] / 1e3,
         "higher_is_better": True,
@@ -398,7 +419,8 @@ def main():
                                         "frac": round(pre["frac_mfma"], 4),
                                         "traffic": profiled_traffic(
                                             "qmm_prefill_int4_g64_M2048_N12288_K4096"),
-                                        "algorithmic_bytes": pre["alg_bytes"]}}
+                                        "algorithmic_bytes": pre["alg_bytes"]},
+                           "cpu_baseline": cpu_pre}
     line["configs"] = [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                        for r in results]
     print(json.dumps(line), flush=True)
@@ -429,6 +451,61 @@ def profiled_traffic(summary):
     return int(rec["traffic_bytes_per_launch"])
 
 
+def calibrate_spin(torch, log, target_us=150.0):
+    """Cycle count for torch.cuda._sleep that keeps the GPU busy about
+    target_us (enough for the host to enqueue an event and a graph)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cycles = 200000
+    torch.cuda._sleep(cycles)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(cycles)
+    e1.record()
+    torch.cuda.synchronize()
+    us = max(e0.elapsed_time(e1) * 1e3, 1.0)
+    out = int(min(max(cycles * target_us / us, 1000), 1e9))
+    log(f"spin: {cycles} cycles took {us:.1f} us; using {out} cycles before each timed replay")
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_prefill(seconds, log):
+    """The oracle on a row sample of the prefill workload (x [2048, 4096],
+    W [12288, 4096] int4 g64): the first 16 rows of x against all of W,
+    called repeatedly; TFLOP/s counts 2 * rows * N * K per call."""
+    import oracle
+    import synth
+
+    M, N, K, rows = 2048, 12288, 4096, 16
+    _, wb = synth.normal((N, K), 0.02, 201, synth.WEIGHT, "bf16")
+    _, xb = synth.normal((M, K), 1.0, 201, synth.ACT, "bf16")
+    wq, sc, bi = oracle.quantize(wb, "bf16", 64, 4)
+    xs = xb[:rows].copy()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantized_matmul(xs, "bf16", wq, sc, bi, True, 64, 4)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    log(f"cpu oracle (prefill sample): {calls} calls in {el:.2f}s on {threads} threads")
+    return {"value": round(2 * rows * N * K * calls / el / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{calls} oracle quantized_matmul calls on rows 0..{rows - 1} of the prefill "
+                      f"x [{M},{K}] against all of W [{N},{K}] int4 g64 (each call dequantizes W "
+                      f"densely, then an fp64 matmul), {el:.1f} s wall"}
+
+
 def cpu_baseline(seconds, log):
     """The oracle on the decode workload, timed on this host's cores."""
     import numpy as np
@@ -451,7 +528,7 @@ def cpu_baseline(seconds, log):
             break
     log(f"cpu oracle: {calls} full decode calls in {el:.2f}s on {threads} threads")
     return {"value": round(alg * calls / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{calls} complete oracle quantized_matmul calls on the decode workload "
                       f"(M1 N{N} K{K} int4 g64), {el:.1f} s wall"}
 

@@ -38,7 +38,8 @@
  *   Microscaled modes have no biases (pass NULL). A (mode, group_size, bits)
  *   mismatch is QLIN_ERR_INVALID_ARGUMENT.
  * - Thread safety: no global mutable state besides the per-thread error
- *   text; concurrent calls on different streams are independent.
+ *   text and last-path record; concurrent calls on different streams are
+ *   independent.
  */
 #ifndef QLIN_H
 #define QLIN_H
@@ -191,8 +192,12 @@ size_t qlin_qqmm_workspace_bytes(int64_t M, int64_t K);
  * fly, W arrives quantized (mlx-rs qqmm: the nvfp4 and mxfp8 modes; the
  * optional global scales are not taken -- one level of scales).
  *   x        bf16 [M, K]; quantized along K with W's mode, group size and
- *            bits by the same rule as qlin_quantize, then decoded back into
- *            the workspace (every decoded value is exact in bf16).
+ *            bits by the same rule as qlin_quantize. mxfp8 with M >= 32
+ *            ([out, in] layout, K a multiple of 512): the workspace receives x's E4M3 codes
+ *            [M, K] and then its E8M0 scales [M, K/32], which the CDNA4
+ *            scaled fp8 MFMA multiplies against W's directly. Otherwise x is
+ *            decoded back into the workspace as bf16 [M, K] (every decoded
+ *            value is exact in bf16) for the bf16 MFMA kernels.
  *   wq, scales  W as for qlin_quantized_matmul in mode "nvfp4" (16, 4) or
  *            "mxfp8" (32, 8); no biases. transpose as there.
  *   workspace   device memory of at least qlin_qqmm_workspace_bytes(M, K)
@@ -233,7 +238,14 @@ size_t qlin_gather_qmm_workspace_bytes(int64_t R, int64_t E);
  *   workspace  device buffer of at least
  *        qlin_gather_qmm_workspace_bytes(R, E) bytes, owned by the caller.
  *   y    out, [R, M, N] of x_dtype (same dtype rule as quantized_matmul).
- * Index values are a precondition (not checked on the device).
+ * Index values are a precondition. The kernels keep their own memory
+ * accesses inside the buffers whatever the indices hold, but the output row
+ * of an index row with rhs >= E or lhs >= B is unspecified (the grouped
+ * kernels leave it unwritten). With the environment variable
+ * QLIN_CHECK_INDICES=1 a small kernel checks every index first, the call
+ * waits for it on the host and returns QLIN_ERR_INVALID_ARGUMENT naming the
+ * first bad row, launching nothing else; under HIP graph capture that check
+ * cannot wait and the call returns QLIN_ERR_UNSUPPORTED.
  */
 qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_t M, int64_t K,
                             const uint32_t* wq, const void* scales, const void* biases,
@@ -245,6 +257,16 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
 
 /* Message describing the calling thread's last failed call ("" if none). */
 const char* qlin_last_error(void);
+
+/*
+ * Kernel path of the calling thread's last matmul-type call that reached a
+ * launch (a static string: "decode", "in_out", "in_out_split",
+ * "in_out_row_blocks", "prefill", "tiled", "generic", "gather_decode",
+ * "gather_prefill", "qqmm_scaled_mfma"; "" before any). "generic" is the fp32 VALU fallback for
+ * shapes the fast kernels do not take, typically an order of magnitude
+ * slower; QLIN_WARN_FALLBACK=1 also prints a line to stderr when it runs.
+ */
+const char* qlin_last_path(void);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     dequantize,
     gather_qmm,
     gather_qmm_workspace_bytes,
+    last_path,
     library_path,
     load_library,
     quantize,

@@ -66,11 +66,17 @@ def load_library():
     lib.qlin_gather_qmm_workspace_bytes.argtypes = [i64, i64]
     lib.qlin_gather_qmm_workspace_bytes.restype = sz
     lib.qlin_last_error.restype = ctypes.c_char_p
+    lib.qlin_last_path.restype = ctypes.c_char_p
     for f in ("qlin_quantize", "qlin_dequantize", "qlin_quantized_matmul", "qlin_quantized_dense",
               "qlin_gather_qmm"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
+
+
+def last_path() -> str:
+    """Kernel path of this thread's last matmul-type call (qlin_last_path)."""
+    return (load_library().qlin_last_path() or b"").decode()
 
 
 def _check(rc: int):
@@ -300,17 +306,10 @@ def gather_qmm_workspace_bytes(R: int, E: int) -> int:
     return int(load_library().qlin_gather_qmm_workspace_bytes(R, E))
 
 
-def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
-               lhs_indices: Optional[torch.Tensor] = None, sorted_indices: bool = False,
-               workspace: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """qlin_gather_qmm: y[r] = x[lhs[r]] . W[rhs[r]]^T (or . W[rhs[r]]).
-
-    x [B, M, K]; qw.value stacks experts on its leading axis; rhs_indices
-    (and lhs_indices, broadcast against it) of any shape S. Returns
-    y of shape S + (M, N). ("EMLX.Quantization", gather_quantized_matmul.)
-    """
-    lib = load_library()
+def _gather_prep(x, qw, rhs_indices, lhs_indices):
+    """Shapes and flattened int32 index arrays of a gather call (no copy
+    when the indices are already contiguous int32 tensors on x's device and
+    lhs, if given, has rhs's shape)."""
     dev = _dev(x)
     if x.dim() != 3 or qw.value.dim() != 3:
         raise ValueError("gather_qmm takes x [B, M, K] and a stacked weight [E, ., .]")
@@ -331,6 +330,21 @@ def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
         rhs = rhs_b.contiguous().reshape(-1)
     else:
         rhs = rhs.contiguous().reshape(-1)
+    return dev, B, M, K, E, N, shape, lhs, rhs
+
+
+def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
+               lhs_indices: Optional[torch.Tensor] = None, sorted_indices: bool = False,
+               workspace: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qlin_gather_qmm: y[r] = x[lhs[r]] . W[rhs[r]]^T (or . W[rhs[r]]).
+
+    x [B, M, K]; qw.value stacks experts on its leading axis; rhs_indices
+    (and lhs_indices, broadcast against it) of any shape S. Returns
+    y of shape S + (M, N). ("EMLX.Quantization", gather_quantized_matmul.)
+    """
+    lib = load_library()
+    dev, B, M, K, E, N, shape, lhs, rhs = _gather_prep(x, qw, rhs_indices, lhs_indices)
     R = rhs.numel()
     need = int(lib.qlin_gather_qmm_workspace_bytes(R, E))
     if workspace is None or workspace.numel() < need:
@@ -343,3 +357,4 @@ def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
                              _ptr(y), _stream(dev))
     _check(rc)
     return y
+

@@ -25,6 +25,20 @@ hipError_t launch_qmm_nt_split(const QmmArgs& q, void* workspace, hipStream_t st
 namespace {
 
 thread_local std::string g_last_error;
+// kernel path of the calling thread's last successful matmul-type call
+thread_local const char* g_last_path = "";
+
+// The generic kernel is the fp32 VALU fallback for shapes the fast kernels
+// refuse; it can be 10-15x slower. QLIN_WARN_FALLBACK=1 prints one line to
+// stderr each time it runs.
+void note_path(const char* p) {
+    g_last_path = p;
+    if (!strcmp(p, "generic")) {
+        const char* e = getenv("QLIN_WARN_FALLBACK");
+        if (e && e[0] == '1' && e[1] == 0)
+            fprintf(stderr, "libqlin: this shape runs on the generic fp32 VALU kernel (slow path)\n");
+    }
+}
 
 qlin_status fail(qlin_status st, const char* fmt, ...) {
     char buf[512];
@@ -35,6 +49,11 @@ qlin_status fail(qlin_status st, const char* fmt, ...) {
     g_last_error = buf;
     return st;
 }
+
+// qqmm in mxfp8 takes the scaled fp8 MFMA kernel from this many rows of x
+// (below it the weight stream bounds the time and the exact bf16 decode
+// kernels serve).
+constexpr int64_t kQqmmScaledMinRows = 32;
 
 qlin_status ok() {
     g_last_error.clear();
@@ -93,7 +112,7 @@ qlin_status check_scale_dtype(int mode, int scale_dtype, const void* biases) {
 }
 
 // Kernel path override for tests of each code path ("generic", "decode",
-// "tiled", "prefill"); unset means automatic choice.
+// "tiled", "prefill", "split", "scaled"); unset means automatic choice.
 int forced_path() {
     const char* e = getenv("QLIN_FORCE_PATH");
     if (!e || !*e) return 0;
@@ -102,23 +121,66 @@ int forced_path() {
     if (!strcmp(e, "tiled")) return 3;
     if (!strcmp(e, "prefill")) return 4;
     if (!strcmp(e, "split")) return 5;
+    if (!strcmp(e, "scaled")) return 7;
     return 0;
+}
+
+// QLIN_CHECK_INDICES=1: before any gather kernel, one small kernel looks for
+// an index row whose expert is >= E or whose batch entry is >= B; the host
+// waits for it and fails the call with that row. The indices are otherwise a
+// precondition (the kernels then only keep their own accesses in range). The
+// wait cannot happen under HIP graph capture, so the check refuses to run there.
+bool index_check_enabled() {
+    const char* e = getenv("QLIN_CHECK_INDICES");
+    return e && e[0] == '1' && e[1] == 0;
+}
+
+qlin_status check_indices_if_asked(const uint32_t* rhs, const uint32_t* lhs, int64_t R, int64_t E,
+                                   int64_t B, void* workspace, hipStream_t s) {
+    if (!index_check_enabled()) return QLIN_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return device_status(e, "gather_qmm (index check)");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(QLIN_ERR_UNSUPPORTED,
+                    "QLIN_CHECK_INDICES=1 waits for the device and cannot run under graph capture");
+    uint32_t* res = qlin::index_check_result(workspace, R, E);
+    if ((e = qlin::launch_check_indices(rhs, lhs, R, E, B, res, s)) != hipSuccess)
+        return device_status(e, "gather_qmm (index check)");
+    uint32_t h[3] = {0, 0, 0};
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return device_status(e, "gather_qmm (index check)");
+    if ((e = hipMemcpy(h, res, sizeof h, hipMemcpyDeviceToHost)) != hipSuccess)
+        return device_status(e, "gather_qmm (index check)");
+    if (h[0] != 0xFFFFFFFFu) {
+        if (h[1] >= (uint64_t)E)
+            return fail(QLIN_ERR_INVALID_ARGUMENT, "rhs_indices[%u] = %u is not below E = %lld",
+                        h[0], h[1], (long long)E);
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "%s[%u] = %u is not below B = %lld",
+                    lhs ? "lhs_indices" : "index row", h[0], h[2], (long long)B);
+    }
+    return QLIN_OK;
 }
 
 qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t* offsets,
                     hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0) {
     const int force = forced_path();
-    if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_decode_supports(a))
+    if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_decode_supports(a)) {
+        note_path("decode");
         return device_status(qlin::launch_qmm_decode(a, st), "quantized_matmul (decode kernel)");
+    }
     if (a.R == 0 && ws && (force == 0 || force == 5)) {
         const size_t need = qlin::qmm_nt_split_workspace_bytes(a);
-        if (need > 0 && ws_bytes >= need)
+        if (need > 0 && ws_bytes >= need) {
+            note_path("in_out_split");
             return device_status(qlin::launch_qmm_nt_split(a, ws, st),
                                  "quantized_matmul ([in,out] K-split kernel)");
+        }
     }
     if (force == 5) return fail(QLIN_ERR_UNSUPPORTED, "K-split kernel does not take this shape or workspace");
-    if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_nt_supports(a))
+    if (a.R == 0 && (force == 0 || force == 2) && qlin::qmm_nt_supports(a)) {
+        note_path("in_out");
         return device_status(qlin::launch_qmm_nt(a, st), "quantized_matmul ([in,out] kernel)");
+    }
     // [in,out] layout with 9..128 rows: the few-row kernel over blocks of 8
     // rows (each block streams W once; M16 at N = K = 8192 mxfp4 takes 2 x 35
     // us instead of 1.5 ms in the generic kernel)
@@ -127,6 +189,7 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
         qlin::QmmArgs c = a;
         c.M = 8;
         if (qlin::qmm_nt_supports(c)) {
+            note_path("in_out_row_blocks");
             for (int64_t m0 = 0; m0 < a.M; m0 += 8) {
                 c.M = a.M - m0 < 8 ? a.M - m0 : 8;
                 c.x = (const char*)a.x + m0 * a.K * 2;
@@ -139,14 +202,19 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
         }
     }
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
-    if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
+    if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a)) {
+        note_path(a.R ? "gather_prefill" : "prefill");
         return device_status(qlin::launch_qmm_prefill(a, perm, offsets, st),
                              a.R ? "gather_qmm (many-row kernel)" : "quantized_matmul (prefill kernel)");
+    }
     if (force == 4) return fail(QLIN_ERR_UNSUPPORTED, "prefill kernel does not take this shape");
-    if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
+    if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a)) {
+        note_path("tiled");
         return device_status(qlin::launch_qmm_tiled(a, perm, offsets, st),
                              "quantized_matmul (tiled kernel)");
+    }
     if (force == 3) return fail(QLIN_ERR_UNSUPPORTED, "tiled kernel does not take this shape");
+    note_path("generic");
     return device_status(qlin::launch_qmm_generic(a, st), "quantized_matmul (generic kernel)");
 }
 
@@ -155,6 +223,8 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
 extern "C" {
 
 const char* qlin_last_error(void) { return g_last_error.c_str(); }
+
+const char* qlin_last_path(void) { return g_last_path; }
 
 qlin_status qlin_quantize(const void* w, qlin_dtype w_dtype, int64_t rows, int64_t cols,
                           int group_size, int bits, const char* mode, uint32_t* wq, void* scales,
@@ -334,6 +404,23 @@ qlin_status qlin_qqmm(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K, c
     if (M > (1LL << 31) || N > (1LL << 31) || K > (1LL << 31))
         return fail(QLIN_ERR_UNSUPPORTED, "dimensions above 2^31 are not supported");
     hipStream_t s = (hipStream_t)stream;
+    // mxfp8 with enough rows: x's codes and scales are the scaled fp8 MFMA's
+    // operands as they are (workspace: M*K code bytes, then M*K/32 scale
+    // bytes), so the product runs at the fp8 rate with no decode at all
+    const int force = forced_path();
+    if (m == qlin::MXFP8 && transpose && (force == 0 || force == 7) && M >= kQqmmScaledMinRows &&
+        qlin::qqmm_mx8_supports(M, N, K, wq, scales)) {
+        uint8_t* xq = (uint8_t*)workspace;
+        uint8_t* xs = xq + M * K;
+        hipError_t e = qlin::launch_quantize(x, QLIN_BF16, M, K, group_size, bits, m, (uint32_t*)xq, xs,
+                                             nullptr, s);
+        if (e != hipSuccess) return device_status(e, "qqmm (activation quantization)");
+        note_path("qqmm_scaled_mfma");
+        return device_status(qlin::launch_qqmm_mx8(xq, xs, (const uint8_t*)wq, (const uint8_t*)scales,
+                                                   (uint16_t*)y, M, N, K, s),
+                             "qqmm (scaled fp8 MFMA kernel)");
+    }
+    if (force == 7) return fail(QLIN_ERR_UNSUPPORTED, "scaled-MFMA qqmm does not take this shape");
     hipError_t e = qlin::launch_qdq_micro(x, M, K, group_size, m, workspace, s);
     if (e != hipSuccess) return device_status(e, "qqmm (activation quantization)");
     qlin::QmmArgs a{};
@@ -412,6 +499,7 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
     a.lhs = lhs_indices;
     a.rhs = rhs_indices;
     hipStream_t s = (hipStream_t)stream;
+    if ((st = check_indices_if_asked(rhs_indices, lhs_indices, R, E, B, workspace, s))) return st;
     uint32_t *perm = nullptr, *offsets = nullptr;
     // the MFMA paths read rows bucketed by expert, in tiles of their own size;
     // few rows per expert (decode) take the small-M kernel's gather form
@@ -430,10 +518,13 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
                                            workspace, &perm, &offsets, s);
         if (e != hipSuccess) return device_status(e, "gather_qmm (expert bucketing)");
     }
-    if (decode_rows != 0)
+    if (decode_rows != 0) {
+        note_path("gather_decode");
         return device_status(qlin::launch_qmm_decode_gather(a, perm, offsets, decode_rows, s),
                              "gather_qmm (decode kernel)");
+    }
     return run_qmm(a, perm, offsets, s);
 }
 
 }  // extern "C"
+

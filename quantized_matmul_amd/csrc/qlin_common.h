@@ -159,6 +159,12 @@ bool qmm_prefill_supports(const QmmArgs& a);
 hipError_t launch_qmm_nt(const QmmArgs& a, hipStream_t s);
 bool qmm_nt_supports(const QmmArgs& a);
 bool qmm_decode_supports(const QmmArgs& a);
+// qqmm in mxfp8 on the scaled fp8 MFMA: x's E4M3 codes [M, K] and E8M0
+// scales [M, K/32] against W's, y bf16 [M, N] (transpose layout).
+bool qqmm_mx8_supports(int64_t M, int64_t N, int64_t K, const void* wq, const void* ws);
+hipError_t launch_qqmm_mx8(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
+                           uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 // Gather form of the small-M kernel (transpose, bf16 x, few rows per
 // expert): rows bucketed by expert into tiles of the returned height, each
 // tile streaming its expert's weight once; -1: far fewer rows than experts,
@@ -174,5 +180,13 @@ hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, i
                          int rows_per_tile, void* workspace, uint32_t** row_perm,
                          uint32_t** expert_offsets, hipStream_t s);
 size_t bucket_workspace_bytes(int64_t R, int64_t E);
+// Opt-in index range check: one small kernel writes, into `result` (3
+// words of device memory), the first index row r with rhs[r] >= E or
+// lhs[r] >= B (r >= B without lhs), or 0xFFFFFFFF, then rhs[r] and lhs[r].
+hipError_t launch_check_indices(const uint32_t* rhs, const uint32_t* lhs, int64_t R, int64_t E,
+                                int64_t B, uint32_t* result, hipStream_t s);
+// Where the check's result lives in a gather workspace of
+// bucket_workspace_bytes(R, E) bytes (16-byte aligned, past the buckets).
+uint32_t* index_check_result(void* workspace, int64_t R, int64_t E);
 
 }  // namespace qlin

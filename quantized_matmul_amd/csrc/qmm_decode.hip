@@ -293,7 +293,9 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
     if (GATHER && !a.perm) {
         // direct form: one index row per tile
         row_begin = blockIdx.y;
-        const int lo = (int)a.rhs[row_begin];
+        const uint32_t ex = a.rhs[row_begin];
+        if (ex >= (uint32_t)a.E) return;             // out-of-range expert: row left unwritten
+        const int lo = (int)ex;
         M = a.Mx;
         const size_t erows = (size_t)lo * (size_t)a.N;   // stacked weight rows before expert lo
         wqp += erows * (size_t)(K / F::PER);

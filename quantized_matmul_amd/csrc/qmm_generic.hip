@@ -49,8 +49,12 @@ __device__ __forceinline__ void row_map(const QmmArgs& a, int64_t rho, int64_t& 
     }
     int64_t r = rho / a.M, m = rho - r * a.M;
     int64_t b = a.lhs ? (int64_t)a.lhs[r] : r;
-    xrow = b * a.M + m;
     expert = a.rhs[r];
+    // indices are a precondition; out-of-range ones read row 0 / expert 0
+    // (that output row is then meaningless) instead of leaving the buffers
+    if (b >= a.batch_x) b = 0;
+    if (expert >= a.E) expert = 0;
+    xrow = b * a.M + m;
 }
 
 constexpr int ROWS_PER_WAVE = 4;

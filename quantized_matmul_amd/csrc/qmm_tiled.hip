@@ -5,7 +5,7 @@
 // ("EMLX.Quantization", quantized_matmul) -- the prefill case, which is a
 // dense contraction -- and its mixture-of-experts form
 // ("EMLX.Quantization", gather_quantized_matmul): rows are bucketed by
-// expert on the device (bucket kernel below) and every expert's weight tile
+// expert on the device (gather_index.hip) and every expert's weight tile
 // is read in place once per row tile, never copied per row.
 //
 // Per K-iteration (64 k) a workgroup of 256 threads:
@@ -61,6 +61,7 @@ struct TiledArgs {
     const uint32_t* offsets; // [E+1] index-row offsets per expert
     const uint32_t* tiles;   // [E+1] row-tile prefix per expert
     int E;
+    int B;                   // activation batch entries (lhs values must be below)
     OutBias ob;              // dense-layer bias (plain form)
 };
 
@@ -203,7 +204,8 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
         if constexpr (GATHER) {
             const int ir = (int)a.perm[row_begin + rho / a.M];
             const int mm = rho % a.M;
-            const int b = a.lhs ? (int)a.lhs[ir] : ir;
+            int b = a.lhs ? (int)a.lhs[ir] : ir;
+            if ((unsigned)b >= (unsigned)a.B) b = 0;   // precondition broken: stay in x
             xrow = b * a.M + mm;
             yrow = ir * a.M + mm;
         } else {
@@ -349,115 +351,6 @@ __global__ void __launch_bounds__(NTHREADS) qmm_tiled_kernel(TiledArgs a) {
     }
 }
 
-// One workgroup: per-expert counts, exclusive scan into offsets and row-tile
-// prefix, then rows placed into expert order (or the identity when the
-// caller's indices are verified non-decreasing). Eight waves; each thread
-// keeps the experts of its first BCACHE rows in registers, so rhs is read
-// once (the kernel is latency-bound: a few barriers and memory round trips).
-#ifndef QLIN_BUCKET_THREADS
-#define QLIN_BUCKET_THREADS 512   // 8 waves: MoE 4096 rows ~1.8 us faster than 4
-#endif
-constexpr int BUCKET_THREADS = QLIN_BUCKET_THREADS;
-// a single wave for few index rows (decode-sized batches): its barriers cost
-// nothing and the one workgroup is all there is to launch
-#ifndef QLIN_BUCKET_SMALL_R
-#define QLIN_BUCKET_SMALL_R 512
-#endif
-
-template <int NTH>
-__global__ void __launch_bounds__(NTH) bucket_kernel(const uint32_t* __restrict__ rhs, int R,
-                                                                int E, int M, int BMrows, int sorted,
-                                                                uint32_t* __restrict__ offsets,
-                                                                uint32_t* __restrict__ tiles,
-                                                                uint32_t* __restrict__ perm) {
-    constexpr int NT = NTH;
-    constexpr int BCACHE = NT >= 512 ? 4096 / NT : 8;   // rows per thread kept in registers
-    extern __shared__ uint32_t sh[];
-    uint32_t* cnt = sh;          // [E]
-    uint32_t* cur = sh + E;      // [E]
-    __shared__ int unsorted;
-    __shared__ uint32_t carry[2];
-    __shared__ uint32_t wsum[NT / 64][2];
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        unsorted = 0;
-        carry[0] = carry[1] = 0;
-    }
-    for (int e = tid; e < E; e += NT) cnt[e] = 0;
-    // rows tid + c * NT, c < BCACHE: experts kept in registers
-    uint32_t rv[BCACHE];
-#pragma unroll
-    for (int c = 0; c < BCACHE; ++c) {
-        const int r = tid + c * NT;
-        rv[c] = r < R ? rhs[r] : 0u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < BCACHE; ++c) {
-        const int r = tid + c * NT;
-        if (r < R) {
-            atomicAdd(&cnt[rv[c]], 1u);
-            if (sorted && r + 1 < R && rv[c] > rhs[r + 1]) unsorted = 1;
-        }
-    }
-    for (int r = tid + BCACHE * NT; r < R; r += NT) {
-        const uint32_t v = rhs[r];
-        atomicAdd(&cnt[v], 1u);
-        if (sorted && r + 1 < R && v > rhs[r + 1]) unsorted = 1;
-    }
-    __syncthreads();
-    // exclusive scans of counts and of row tiles, in chunks of NT experts
-    for (int base = 0; base < E; base += NT) {
-        const int e = base + tid;
-        const uint32_t c = e < E ? cnt[e] : 0u;
-        const uint32_t t = (uint32_t)(((uint64_t)c * M + BMrows - 1) / BMrows);
-        uint32_t vc = c, vt = t;
-        // inclusive wave scans, then across waves through shared memory
-        for (int off = 1; off < 64; off <<= 1) {
-            uint32_t uc = __shfl_up(vc, off, 64), ut = __shfl_up(vt, off, 64);
-            if ((tid & 63) >= off) {
-                vc += uc;
-                vt += ut;
-            }
-        }
-        if ((tid & 63) == 63) {
-            wsum[tid >> 6][0] = vc;
-            wsum[tid >> 6][1] = vt;
-        }
-        __syncthreads();
-        uint32_t pc = carry[0], pt = carry[1];
-        for (int w = 0; w < (tid >> 6); ++w) {
-            pc += wsum[w][0];
-            pt += wsum[w][1];
-        }
-        if (e < E) {
-            offsets[e] = pc + vc - c;
-            tiles[e] = pt + vt - t;
-            cur[e] = pc + vc - c;
-        }
-        __syncthreads();
-        if (tid == NT - 1) {
-            carry[0] = pc + vc;
-            carry[1] = pt + vt;
-        }
-        __syncthreads();
-    }
-    if (tid == 0) {
-        offsets[E] = carry[0];
-        tiles[E] = carry[1];
-    }
-    if (sorted && !unsorted) {
-        for (int r = tid; r < R; r += NT) perm[r] = (uint32_t)r;
-    } else {
-#pragma unroll
-        for (int c = 0; c < BCACHE; ++c) {
-            const int r = tid + c * NT;
-            if (r < R) perm[atomicAdd(&cur[rv[c]], 1u)] = (uint32_t)r;
-        }
-        for (int r = tid + BCACHE * NT; r < R; r += NT) perm[atomicAdd(&cur[rhs[r]], 1u)] = (uint32_t)r;
-    }
-}
-
 template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, bool GATHER>
 hipError_t launch_cfg(const TiledArgs& t, int grid, hipStream_t st) {
     const size_t shm = (size_t)2 * (BM + BN) * LROW;
@@ -500,6 +393,7 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     t.offsets = offsets;
     t.tiles = offsets + (q.E + 1);
     t.E = (int)q.E;
+    t.B = (int)q.batch_x;
     constexpr int BM = GATHER_BM, BN = 256;
     // upper bound on row tiles: every expert may add one partial tile
     const int64_t mt = (q.R * q.M + BM - 1) / BM + q.E;
@@ -515,30 +409,6 @@ bool qmm_tiled_supports(const QmmArgs& q) {
     if (q.R > 0 && (q.E > 8192 || q.R * q.M >= (1LL << 30))) return false;
     if (((uintptr_t)q.wq & 15) || ((uintptr_t)q.x & 15)) return false;
     return true;
-}
-
-size_t bucket_workspace_bytes(int64_t R, int64_t E) {
-    // offsets [E+1], tiles [E+1], perm [R]
-    return (size_t)(2 * (E + 1) + R) * sizeof(uint32_t) + 256;
-}
-
-hipError_t launch_bucket(const uint32_t* rhs, int64_t R, int64_t E, int64_t M, int sorted,
-                         int rows_per_tile, void* workspace, uint32_t** perm, uint32_t** offsets,
-                         hipStream_t st) {
-    uint32_t* ws = (uint32_t*)workspace;
-    *offsets = ws;                   // [E+1] then tiles [E+1]
-    *perm = ws + 2 * (E + 1);
-    const size_t shm = (size_t)2 * E * sizeof(uint32_t);
-    if (shm > 64 * 1024) return hipErrorInvalidValue;
-    if (rows_per_tile < 1) return hipErrorInvalidValue;
-    if (R <= QLIN_BUCKET_SMALL_R)
-        bucket_kernel<64><<<1, 64, shm, st>>>(rhs, (int)R, (int)E, (int)M, rows_per_tile, sorted,
-                                              *offsets, *offsets + (E + 1), *perm);
-    else
-        bucket_kernel<BUCKET_THREADS><<<1, BUCKET_THREADS, shm, st>>>(rhs, (int)R, (int)E, (int)M,
-                                                                      rows_per_tile, sorted, *offsets,
-                                                                      *offsets + (E + 1), *perm);
-    return hipGetLastError();
 }
 
 hipError_t launch_qmm_tiled(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,

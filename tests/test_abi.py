@@ -196,3 +196,7 @@ def test_gather_rejects(lib):
     assert call(E=0) == INVALID
     assert call(mode=b"mxfp8", g=32, bits=8, sdt=U8, b=None, K=100) == INVALID
     assert call(R=0, B=0) == 0                  # empty: no-op
+
+
+def test_last_path_is_exported(lib):
+    assert lib.qlin_last_path() is not None

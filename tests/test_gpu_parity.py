@@ -689,6 +689,16 @@ QQMM_CASES = [
     (7, 128, 256, "nvfp4", True, "generic"),
 ]
 
+# mxfp8 on the scaled fp8 MFMA (the workspace holds x's codes and scales)
+QQMM_SCALED_CASES = [
+    # M, N, K
+    (32, 128, 512),          # one tile, one batch of 4 K steps
+    (300, 384, 512),         # ragged rows, several tiles
+    (130, 200, 1024),        # ragged weight rows (N % 4 != 0 columns stored one by one)
+    (512, 1024, 2048),
+    (64, 256, 8192),         # long K
+]
+
 
 @pytest.mark.parametrize("case", QQMM_CASES, ids=lambda c: f"M{c[0]}N{c[1]}K{c[2]}{c[3]}t{int(c[4])}{c[5]}")
 def test_qqmm(case):
@@ -712,3 +722,29 @@ def test_qqmm(case):
     print(f"qqmm {case}: err {err:.3e}", flush=True)
     assert err <= 4e-3
 
+
+
+@pytest.mark.parametrize("case", QQMM_SCALED_CASES, ids=lambda c: f"M{c[0]}N{c[1]}K{c[2]}")
+def test_qqmm_scaled_mfma(case):
+    """mlx-rs qqmm in mxfp8 on v_mfma_scale_f32_32x32x64_f8f6f4: x's codes
+    and scale bytes in the workspace bit-exact against the oracle's
+    quantization of x, y within the qqmm bar of the oracle's product."""
+    M, N, K = case
+    g, bits = 32, 8
+    w, wb = gpu_weight((N, K), 0.02, 52, "bf16")
+    xt, xb = synth.normal((M, K), 1.0, 52, synth.ACT, "bf16")
+    qw, (wq, sc, _) = quantize_both(w, wb, "bf16", g, bits, "mxfp8", True)
+    ws = torch.empty(qm.qqmm_workspace_bytes(M, K), dtype=torch.uint8, device=DEV)
+    os.environ["QLIN_FORCE_PATH"] = "scaled"
+    y = qm.qqmm(xt.to(DEV), qw, workspace=ws)
+    torch.cuda.synchronize()
+    os.environ.pop("QLIN_FORCE_PATH", None)
+    assert qm.last_path() == "qqmm_scaled_mfma"
+    xq, xs, _ = oracle.quantize(xb, "bf16", g, bits, "mxfp8")
+    got = ws.cpu().numpy()
+    assert np.array_equal(got[:M * K], xq.view(np.uint8).reshape(-1))
+    assert np.array_equal(got[M * K:M * K + M * K // 32], xs.reshape(-1))
+    yref = oracle.qqmm(xb, "bf16", wq, sc, True, g, bits, "mxfp8")
+    err = normwise_rel_err(y, yref)
+    print(f"qqmm scaled M{M} N{N} K{K}: err {err:.3e}", flush=True)
+    assert err <= 4e-3
