@@ -255,6 +255,30 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
                             int sorted_indices, void* workspace, size_t workspace_bytes, void* y,
                             void* stream);
 
+/*
+ * qlin_gather_qmm_noalloc -- qlin_gather_qmm without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The call
+ * allocates nothing; the bucketing scratch is a fixed device array inside
+ * the library (about 295 KB per GPU, held until the process ends), which
+ * limits the problem to R <= qlin_gather_qmm_noalloc_max_rows() (65536)
+ * index rows and E <= qlin_gather_qmm_noalloc_max_experts() (4096) experts;
+ * larger ones return QLIN_ERR_INVALID_ARGUMENT before anything runs (use
+ * qlin_gather_qmm with a workspace). Every call on one GPU uses that GPU's
+ * array: calls that overlap in time on the same GPU (other streams or
+ * threads) race on it and must be serialised by the caller. Arguments,
+ * results and errors are otherwise those of qlin_gather_qmm.
+ */
+qlin_status qlin_gather_qmm_noalloc(const void* x, qlin_dtype x_dtype, int64_t B, int64_t M,
+                                    int64_t K, const uint32_t* wq, const void* scales,
+                                    const void* biases, qlin_dtype scale_dtype, int64_t E,
+                                    int64_t N, const uint32_t* lhs_indices,
+                                    const uint32_t* rhs_indices, int64_t R, int transpose,
+                                    int group_size, int bits, const char* mode, int sorted_indices,
+                                    void* y, void* stream);
+size_t qlin_gather_qmm_noalloc_max_rows(void);
+size_t qlin_gather_qmm_noalloc_max_experts(void);
+
 /* Message describing the calling thread's last failed call ("" if none). */
 const char* qlin_last_error(void);
 

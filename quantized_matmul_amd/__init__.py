@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     QuantizedWeight,
     dequantize,
     gather_qmm,
+    gather_qmm_noalloc,
     gather_qmm_workspace_bytes,
     last_path,
     library_path,

@@ -65,6 +65,11 @@ def load_library():
     lib.qlin_qqmm_workspace_bytes.restype = sz
     lib.qlin_gather_qmm_workspace_bytes.argtypes = [i64, i64]
     lib.qlin_gather_qmm_workspace_bytes.restype = sz
+    lib.qlin_gather_qmm_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64,
+                                            vp, vp, i64, i32, i32, i32, cs, i32, vp, vp]
+    lib.qlin_gather_qmm_noalloc.restype = i32
+    lib.qlin_gather_qmm_noalloc_max_rows.restype = sz
+    lib.qlin_gather_qmm_noalloc_max_experts.restype = sz
     lib.qlin_last_error.restype = ctypes.c_char_p
     lib.qlin_last_path.restype = ctypes.c_char_p
     for f in ("qlin_quantize", "qlin_dequantize", "qlin_quantized_matmul", "qlin_quantized_dense",
@@ -358,3 +363,23 @@ def gather_qmm(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
     _check(rc)
     return y
 
+
+def gather_qmm_noalloc(x: torch.Tensor, qw: QuantizedWeight, rhs_indices: torch.Tensor,
+                       lhs_indices: Optional[torch.Tensor] = None, sorted_indices: bool = False,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qlin_gather_qmm_noalloc: gather_qmm with the library's own fixed
+    scratch instead of a workspace (at most 65536 index rows and 4096
+    experts). The C call allocates nothing; this wrapper allocates only y
+    when `out` is not given and index copies when the indices are not
+    contiguous int32 tensors of one shape on x's device."""
+    lib = load_library()
+    dev, B, M, K, E, N, shape, lhs, rhs = _gather_prep(x, qw, rhs_indices, lhs_indices)
+    R = rhs.numel()
+    y = _out(out, shape + (M, N), x.dtype, dev)
+    rc = lib.qlin_gather_qmm_noalloc(_ptr(x), _DTYPE[x.dtype], B, M, K, _ptr(qw.value),
+                                     _ptr(qw.scales), _ptr(qw.biases), _DTYPE[qw.scales.dtype], E,
+                                     N, _ptr(lhs), _ptr(rhs), R, int(qw.transpose), qw.group_size,
+                                     qw.bits, qw.mode.encode(), int(bool(sorted_indices)), _ptr(y),
+                                     _stream(dev))
+    _check(rc)
+    return y

@@ -11,6 +11,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "../../include/qlin.h"
@@ -528,3 +530,84 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
 
 }  // extern "C"
 
+// ------------------------------------------------------------------------
+// gather_qmm without a caller's workspace, for callers that cannot allocate
+// device memory (code under HIP graph capture, tight serving loops,
+// harnesses that forbid hipMalloc). The bucketing scratch (row permutation,
+// expert offsets, row-tile prefix, index-check result) lives in a
+// file-scope device array of fixed size; every GPU holds its own copy until
+// the process ends. Calls on one GPU share that array: calls that overlap
+// in time on one GPU (different streams, or threads) race on it.
+
+namespace {
+
+constexpr int64_t kNoAllocMaxRows = 65536;      // index rows R
+constexpr int64_t kNoAllocMaxExperts = 4096;    // experts E
+constexpr size_t kScratchBytes =                 // bucket_workspace_bytes(R max, E max)
+    (size_t)(2 * (kNoAllocMaxExperts + 1) + kNoAllocMaxRows) * sizeof(uint32_t) + 256;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array, looked up once per device
+// with that device current (the array's host-side name is not a device
+// address).
+qlin_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "gather_qmm_noalloc (current device)");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QLIN_ERR_UNSUPPORTED, "device ordinal %d above the %d this library tracks", dev,
+                    kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return device_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                     "gather_qmm_noalloc (scratch address)");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QLIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qlin_gather_qmm_noalloc_max_rows(void) { return (size_t)kNoAllocMaxRows; }
+size_t qlin_gather_qmm_noalloc_max_experts(void) { return (size_t)kNoAllocMaxExperts; }
+
+qlin_status qlin_gather_qmm_noalloc(const void* x, qlin_dtype x_dtype, int64_t B, int64_t M,
+                                    int64_t K, const uint32_t* wq, const void* scales,
+                                    const void* biases, qlin_dtype scale_dtype, int64_t E,
+                                    int64_t N, const uint32_t* lhs_indices,
+                                    const uint32_t* rhs_indices, int64_t R, int transpose,
+                                    int group_size, int bits, const char* mode, int sorted_indices,
+                                    void* y, void* stream) {
+    if (R > kNoAllocMaxRows || E > kNoAllocMaxExperts)
+        return fail(QLIN_ERR_INVALID_ARGUMENT,
+                    "gather_qmm_noalloc takes at most %lld index rows and %lld experts "
+                    "(got %lld and %lld); use qlin_gather_qmm with a workspace",
+                    (long long)kNoAllocMaxRows, (long long)kNoAllocMaxExperts, (long long)R,
+                    (long long)E);
+    if (R < 0 || E <= 0 || qlin::bucket_workspace_bytes(R, E) > kScratchBytes)
+        return fail(QLIN_ERR_INVALID_ARGUMENT, "negative size or no experts");
+    void* ws = nullptr;   // an empty problem returns before the workspace is looked at
+    if (R > 0 && M > 0) {
+        qlin_status st = scratch_for_current_device(&ws);
+        if (st) return st;
+    }
+    return qlin_gather_qmm(x, x_dtype, B, M, K, wq, scales, biases, scale_dtype, E, N, lhs_indices,
+                           rhs_indices, R, transpose, group_size, bits, mode, sorted_indices, ws,
+                           kScratchBytes, y, stream);
+}
+
+}  // extern "C"

@@ -198,5 +198,20 @@ def test_gather_rejects(lib):
     assert call(R=0, B=0) == 0                  # empty: no-op
 
 
+def test_gather_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The allocation-free gather refuses problems its fixed scratch cannot
+    hold, before touching any pointer or the device."""
+    assert lib.qlin_gather_qmm_noalloc_max_rows() == 65536
+    assert lib.qlin_gather_qmm_noalloc_max_experts() == 4096
+    args = lambda R, E: (FAKE, BF16, R, 1, 512, FAKE, FAKE, FAKE, BF16, E, 256, None, FAKE, R, 1,
+                         64, 4, b"affine", 0, FAKE, None)
+    assert lib.qlin_gather_qmm_noalloc(*args(65537, 64)) == INVALID
+    assert "at most 65536 index rows" in err(lib)
+    assert lib.qlin_gather_qmm_noalloc(*args(16, 4097)) == INVALID
+    # empty problem: a no-op that needs no scratch
+    assert lib.qlin_gather_qmm_noalloc(FAKE, BF16, 0, 1, 512, FAKE, FAKE, FAKE, BF16, 8, 256, None,
+                                       FAKE, 0, 1, 64, 4, b"affine", 0, FAKE, None) == 0
+
+
 def test_last_path_is_exported(lib):
     assert lib.qlin_last_path() is not None
