@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_obj")
 LIB = os.path.join(HERE, "libqlin.so")
 SOURCES = ["qlin_api.cpp", "quant.hip", "qmm_generic.hip", "qmm_decode.hip", "qmm_tiled.hip", "qmm_nt.hip",
-           "qmm_prefill.hip", "gather_index.hip", "qqmm_mx8.hip"]
+           "qmm_prefill.hip", "qmm_prefill2.hip", "gather_index.hip", "qqmm_mx8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

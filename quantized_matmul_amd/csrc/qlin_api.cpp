@@ -19,6 +19,27 @@
 #include "qlin_common.h"
 
 namespace qlin {
+
+DeviceShape device_shape() {
+    // one entry per device id; a racing first call on one device at worst
+    // queries twice and stores the same values
+    static std::atomic<int> cus[64], xcds[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceShape{256, 8};
+    int c = cus[dev].load(std::memory_order_acquire);
+    int x = xcds[dev].load(std::memory_order_acquire);
+    if (c <= 0 || x <= 0) {
+        c = 0;
+        x = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0) x = 1;
+        xcds[dev].store(x, std::memory_order_release);
+        cus[dev].store(c, std::memory_order_release);
+    }
+    return DeviceShape{c, x};
+}
+
 // [in, out] layout with a caller's workspace (K split over workgroups)
 size_t qmm_nt_split_workspace_bytes(const QmmArgs& q);
 hipError_t launch_qmm_nt_split(const QmmArgs& q, void* workspace, hipStream_t st);
@@ -114,7 +135,8 @@ qlin_status check_scale_dtype(int mode, int scale_dtype, const void* biases) {
 }
 
 // Kernel path override for tests of each code path ("generic", "decode",
-// "tiled", "prefill", "split", "scaled"); unset means automatic choice.
+// "tiled", "prefill", "prefill2", "split", "scaled"); unset means automatic
+// choice.
 int forced_path() {
     const char* e = getenv("QLIN_FORCE_PATH");
     if (!e || !*e) return 0;
@@ -124,6 +146,7 @@ int forced_path() {
     if (!strcmp(e, "prefill")) return 4;
     if (!strcmp(e, "split")) return 5;
     if (!strcmp(e, "scaled")) return 7;
+    if (!strcmp(e, "prefill2")) return 8;
     return 0;
 }
 
@@ -204,6 +227,13 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
         }
     }
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
+    if (a.R == 0 && (force == 8 || (force == 0 && a.M >= qlin::kPrefill2MinRows)) &&
+        qlin::qmm_prefill2_supports(a)) {
+        note_path("prefill2");
+        return device_status(qlin::launch_qmm_prefill2(a, st),
+                             "quantized_matmul (pipelined 4-bit prefill kernel)");
+    }
+    if (force == 8) return fail(QLIN_ERR_UNSUPPORTED, "pipelined 4-bit prefill kernel does not take this shape");
     if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a)) {
         note_path(a.R ? "gather_prefill" : "prefill");
         return device_status(qlin::launch_qmm_prefill(a, perm, offsets, st),

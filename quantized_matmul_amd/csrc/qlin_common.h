@@ -9,6 +9,24 @@
 
 namespace qlin {
 
+// Compute units and XCDs (accelerator dies, each with its own L2) of the
+// current device, queried once per device. Workgroups are dealt to the XCDs
+// round-robin, so kernels that share data between neighbouring tiles
+// renumber their blocks so that each XCD walks a contiguous run.
+struct DeviceShape {
+    int cus;
+    int xcds;
+};
+DeviceShape device_shape();
+
+// Renumbers block b of nblk so that XCD x (= b % xcds) takes the contiguous
+// run [x * nblk / xcds, (x + 1) * nblk / xcds); a bijection when xcds divides
+// nblk, the identity otherwise.
+__device__ __forceinline__ int xcd_block(int b, int nblk, int xcds) {
+    if (xcds <= 1 || nblk % xcds != 0) return b;
+    return (b % xcds) * (nblk / xcds) + b / xcds;
+}
+
 enum Mode : int { AFFINE = 0, MXFP4 = 1, MXFP8 = 2, NVFP4 = 3 };
 
 // ---------------------------------------------------------------- dtype I/O
@@ -147,14 +165,18 @@ bool qmm_tiled_supports(const QmmArgs& a);
 // MFMA path for many rows (transpose, bf16 x), plain or expert-gathered:
 // the weight tile is dequantized once into LDS per tile of activation rows.
 // The gather form needs the bucketing below, run with kPrefillGatherRows.
-#ifndef QLIN_PREFILL_GATHER_ROWS
-#define QLIN_PREFILL_GATHER_ROWS 64
-#endif
-constexpr int kPrefillGatherRows = QLIN_PREFILL_GATHER_ROWS;
+constexpr int kPrefillGatherRows = 64;
 constexpr int kTiledGatherRows = 64;   // row tile of the LDS-tiled gather kernel
 hipError_t launch_qmm_prefill(const QmmArgs& a, const uint32_t* row_perm,
                               const uint32_t* expert_offsets, hipStream_t s);
 bool qmm_prefill_supports(const QmmArgs& a);
+// Software-pipelined MFMA path for many rows of 4-bit affine weights
+// (transpose, bf16 x, K a multiple of 256): the weight is dequantized in
+// registers straight into the MFMA operand. Taken by default from
+// kPrefill2MinRows rows on.
+constexpr int64_t kPrefill2MinRows = int64_t(1) << 62;
+hipError_t launch_qmm_prefill2(const QmmArgs& a, hipStream_t s);
+bool qmm_prefill2_supports(const QmmArgs& a);
 // VALU path for the [in, out] layout (transpose = false), M <= 8, bf16 x.
 hipError_t launch_qmm_nt(const QmmArgs& a, hipStream_t s);
 bool qmm_nt_supports(const QmmArgs& a);

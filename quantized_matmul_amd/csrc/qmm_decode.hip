@@ -695,27 +695,20 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
 // Decomposition: a wave's slice is KW = UPW units (choose_upw below); a
 // workgroup has KS = nunits / UPW <= 16 waves. Shorter slices (more waves per
 // workgroup) measured faster: UPW 4 beats 8 by about 5 % at M = 1.
-#ifndef QLIN_DECODE_UPW_MAX
-#define QLIN_DECODE_UPW_MAX 4   // units per wave (power of two, <= 16)
-#endif
-#ifndef QLIN_DECODE_PF
-#define QLIN_DECODE_PF 4        // weight units in flight per wave
-#endif
+constexpr int kDecodeUpwMax = 4;   // units per wave (power of two, <= 16)
+constexpr int kDecodePf = 4;       // weight units in flight per wave
 
 // Output columns per workgroup: all workgroups of a launch are resident at
-// once, so a CU's share is ceil(workgroups / 256) of them; take the widest
+// once, so a CU's share is ceil(workgroups / CUs) of them; take the widest
 // block (at most the 16 MFMA columns) that minimises the columns per CU.
-// N = 14336: 14 columns, 1024 workgroups, 4 per CU (16 columns would give
-// half the CUs 4 workgroups and half 3).
-#ifndef QLIN_DECODE_CUS
-#define QLIN_DECODE_CUS 256
-#endif
-int decode_columns(int N) {
+// N = 14336 on 256 CUs: 14 columns, 1024 workgroups, 4 per CU (16 columns
+// would give half the CUs 4 workgroups and half 3).
+int decode_columns(int N, int cus) {
     int best = 16;
     int64_t best_load = 0;
     for (int c = 16; c >= 8; --c) {
         const int64_t wgs = (N + c - 1) / c;
-        const int64_t load = (wgs + QLIN_DECODE_CUS - 1) / QLIN_DECODE_CUS * c;
+        const int64_t load = (wgs + cus - 1) / cus * c;
         if (c == 16 || load < best_load) {
             best = c;
             best_load = load;
@@ -724,13 +717,13 @@ int decode_columns(int N) {
     return best;
 }
 
-// Units per wave: start from QLIN_DECODE_UPW_MAX (half that for two-region
+// Units per wave: start from kDecodeUpwMax (half that for two-region
 // units), grow while the workgroup would need more than 16 waves, then
 // shrink until it divides the unit count and (staged path) the wave's x
 // slice fits 8 chunk registers per lane. 0: no valid decomposition.
 int choose_upw(int nunits, int64_t M, int U, int RPU, bool dx) {
     const int64_t xlim = dx ? (1LL << 40) : 4096;
-    int upw = RPU >= 2 ? QLIN_DECODE_UPW_MAX / 2 : QLIN_DECODE_UPW_MAX;
+    int upw = RPU >= 2 ? kDecodeUpwMax / 2 : kDecodeUpwMax;
     if (upw < 1) upw = 1;
     while (upw < 16 && nunits / upw > 16) upw <<= 1;
     while (upw > 1 && (nunits % upw || M * upw * U > xlim)) upw >>= 1;
@@ -748,7 +741,7 @@ int pick_upw(int nunits, int M, bool dx) {
 // (an upper bound; tiles past the real count leave at once).
 template <int MODE, int BITS, int G, int UPW, bool DX, int CB = 1>
 hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, hipStream_t st) {
-    constexpr int PF = UPW < QLIN_DECODE_PF ? UPW : QLIN_DECODE_PF;
+    constexpr int PF = UPW < kDecodePf ? UPW : kDecodePf;
     if (CB == 2 && ks > 8) return hipErrorNotSupported;   // 512-thread kernels
     const unsigned blocks = (unsigned)((a.N + a.cols * CB - 1) / (a.cols * CB));
     const dim3 grid(blocks, gather_tiles > 0 ? (unsigned)gather_tiles : 1u);
@@ -811,7 +804,8 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
-    a.cols = decode_columns(a.N);
+    const int cus = device_shape().cus;
+    a.cols = decode_columns(a.N, cus);
     int gather_tiles = 0;
     if (tile_rows < 0) {
         // direct gather form: one tile per index row, its rows = x rows per index row
@@ -839,41 +833,29 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
         a.xrows = (int)(q.batch_x * q.M);
         gather_tiles = (int)(rows / tile_rows + (q.E < q.R ? q.E : q.R));
     }
-#ifndef QLIN_GATHER_COLS16
-#define QLIN_GATHER_COLS16 1
-#endif
     // the gather grid spans many row tiles (several rounds of workgroups):
     // full 16-column blocks halve the workgroups and their fixed costs
-    if (gather_tiles > 0 && QLIN_GATHER_COLS16) a.cols = 16;
+    if (gather_tiles > 0) a.cols = 16;
     const int mreg = a.M > 4 ? 4 : a.M;
     const int nunits = a.K / F::U;
     const int upw = pick_upw<MODE, BITS, G>(nunits, a.M, DX);
     if (upw == 0) return hipErrorNotSupported;
     const int ks = nunits / upw;
-#ifndef QLIN_DECODE_DX_CB
-#define QLIN_DECODE_DX_CB 2
-#endif
-#ifndef QLIN_DECODE_STAGED_CB2_MIN_M
-#define QLIN_DECODE_STAGED_CB2_MIN_M 2
-#endif
     // two column blocks per wave (at most 8 waves: longer slices): direct x
-    // fragments always; staged x from QLIN_DECODE_STAGED_CB2_MIN_M rows up,
+    // fragments always; staged x from two rows up,
     // where every workgroup re-reading all of x from L2 rivals the weight
     // stream (M8: 64 KB of x per workgroup against 56 KB of weights), and
     // for 8-bit affine codes at one row too (M1 int8 15.5 -> 13.9 us; 4-bit
     // and microscaled one-row shapes measured slower this way)
-#ifndef QLIN_GATHER_CB2
-#define QLIN_GATHER_CB2 1
-#endif
-    const bool staged_cb2 = a.M >= QLIN_DECODE_STAGED_CB2_MIN_M || (F::AFF && BITS == 8);
+    const bool staged_cb2 = a.M >= 2 || (F::AFF && BITS == 8);
     // gather form: two blocks per wave share the tile's expert lookup, index
     // loads and x (2 tokens x top-8 10.1 -> 9.5 us, 8 tokens 27.6 -> 23.7 us,
     // 16 tokens 37.7 -> 31.5 us) while the grid keeps two workgroups per CU
     // (1 token: 8 tiles would leave 384 workgroups, 7.2 -> 7.7 us)
-    const bool gather_cb2 = QLIN_GATHER_CB2 && gather_tiles > 0 &&
+    const bool gather_cb2 = gather_tiles > 0 &&
                             (int64_t)gather_tiles * ((a.N + 2 * a.cols - 1) / (2 * a.cols)) >=
-                                2 * QLIN_DECODE_CUS;
-    if ((DX && QLIN_DECODE_DX_CB == 2) || (!DX && gather_tiles == 0 && staged_cb2) ||
+                                2 * (int64_t)cus;
+    if (DX || (!DX && gather_tiles == 0 && staged_cb2) ||
         (!DX && gather_cb2)) {
         int upw2 = upw;
         while (upw2 < 16 && nunits / upw2 > 8) upw2 <<= 1;
@@ -881,7 +863,7 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
         const bool fits = DX || (int64_t)a.M * upw2 * F::U <= 4096;
         if (fits && nunits % upw2 == 0 && nunits / upw2 <= 8) {
             DecodeArgs a2 = a;
-            if (gather_tiles <= 0) a2.cols = decode_columns((a.N + 1) / 2);
+            if (gather_tiles <= 0) a2.cols = decode_columns((a.N + 1) / 2, cus);
             const int ks2 = nunits / upw2;
             switch (upw2) {
             case 16: return launch_upw<MODE, BITS, G, 16, DX, 2>(a2, ks2, mreg, gather_tiles, st);

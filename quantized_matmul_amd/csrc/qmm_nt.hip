@@ -35,6 +35,7 @@ struct NtArgs {
     const uint16_t* biases;
     uint16_t* y;         // bf16 [M, N]
     int M, N, K;
+    int xcds;            // XCDs of the device (block renumbering)
     OutBias ob;          // dense-layer bias
 };
 
@@ -105,13 +106,12 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
     const int rr = lane / LPR, cl = lane % LPR;
     const int K = a.K, N = a.N;
     const int wcols = N / PER;                        // packed words per W row
-    // Workgroups are dealt to the 8 XCDs round-robin. Neighbouring column
+    // Workgroups are dealt to the XCDs round-robin. Neighbouring column
     // blocks share 128-byte lines of every weight row (a block uses WPB words
     // of a row), so renumber the blocks: each XCD walks a contiguous run of
     // them and the shared lines meet in that XCD's L2 instead of being
     // fetched once per XCD.
-    int cb = blockIdx.x;
-    if ((gridDim.x & 7) == 0) cb = (cb & 7) * (gridDim.x >> 3) + (cb >> 3);
+    const int cb = xcd_block(blockIdx.x, gridDim.x, a.xcds);
     const int c = cb * WPB + cl * VW;                 // first word column of the lane
     const bool active = c < wcols;
     const int gpr = N / G;                            // groups per W row
@@ -271,22 +271,15 @@ __global__ void __launch_bounds__(64 * NW) qmm_nt_kernel(NtArgs a) {
 // activation rows rounded up to the kernel's MR (1, 2, 4 or 8)
 inline int nt_mr(int M) { return M <= 2 ? M : (M <= 4 ? 4 : 8); }
 
-#ifndef QLIN_NT_WPB
-#define QLIN_NT_WPB 8
-#endif
-#ifndef QLIN_NT_NW
-#define QLIN_NT_NW 16
-#endif
-#ifndef QLIN_NT_WIDE
-#define QLIN_NT_WIDE 1
-#endif
+constexpr int kNtWpb = 8;    // packed words of a weight row per workgroup
+constexpr int kNtNw = 16;    // waves per workgroup (up to 4 activation rows)
 
 // waves per workgroup: 16 for up to 4 activation rows, 8 for more (the
 // register ring then holds more accumulators per lane)
-inline int nt_waves(int M) { return nt_mr(M) == 8 ? 8 : QLIN_NT_NW; }
+inline int nt_waves(int M) { return nt_mr(M) == 8 ? 8 : kNtNw; }
 
 inline size_t nt_shm(int M, int K, int per) {
-    const int wpb = QLIN_NT_WPB;
+    const int wpb = kNtWpb;
     const size_t red_bytes = (size_t)nt_waves(M) * wpb * per * 4;
     const size_t stage = (size_t)nt_mr(M) * K * 2;
     return stage > red_bytes ? stage : red_bytes;
@@ -304,9 +297,10 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
+    a.xcds = device_shape().xcds;
     constexpr int PER = 32 / BITS;
     const int wcols = a.N / PER;
-    constexpr int WPB = QLIN_NT_WPB, NW = QLIN_NT_NW;
+    constexpr int WPB = kNtWpb, NW = kNtNw;
     const unsigned blocks = (unsigned)((wcols + WPB - 1) / WPB);
     const size_t shm = nt_shm(a.M, a.K, PER);
     auto run = [&](auto kern, int nw) -> hipError_t {
@@ -329,7 +323,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     constexpr int VWIDE = (G / PER) < VCAP ? (G / PER) : VCAP;
     constexpr bool WIDE_FMT = VWIDE > 1 && (MODE != AFFINE || BITS == 2);
     if constexpr (WIDE_FMT) {
-        const bool wide = QLIN_NT_WIDE && a.M == 1 &&
+        const bool wide = a.M == 1 &&
                           ((uintptr_t)a.wq % (4 * VWIDE)) == 0 && (wcols % VWIDE) == 0;
         if (wide) return run(qmm_nt_kernel<MODE, BITS, G, 1, WPB, NW, VWIDE>, NW);
     }
@@ -349,16 +343,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
 // kernel adds the slices in order and writes y. Each workgroup then asks the
 // L2 for a few hundred rows instead of all K, four requests per 256 bytes
 // instead of three per 32.
-#ifndef QLIN_SPLIT_SBW
-#define QLIN_SPLIT_SBW 64
-#endif
-#ifndef QLIN_SPLIT_WGS
-#define QLIN_SPLIT_WGS 256
-#endif
-#ifndef QLIN_SPLIT_RING
-#define QLIN_SPLIT_RING 8
-#endif
-constexpr int SPLIT_SBW = QLIN_SPLIT_SBW;   // packed words per superblock row
+constexpr int SPLIT_SBW = 64;   // packed words per superblock row
 constexpr int SPLIT_NW = 8;                 // waves per workgroup
 
 template <int MODE, int BITS, int G, int MR, int VW>
@@ -370,7 +355,7 @@ __global__ void __launch_bounds__(64 * SPLIT_NW) qmm_nt_split_kernel(NtArgs a, f
     constexpr int LPR = SBW / VW;        // lanes per row
     constexpr int RPS = 64 / LPR;        // rows per wave load
     constexpr int CPL = VW * PER;        // columns per lane
-    constexpr int RING = QLIN_SPLIT_RING;   // wave loads in flight per lane
+    constexpr int RING = 8;   // wave loads in flight per lane
     constexpr bool AFF = MODE == AFFINE;
     constexpr int SBYTES = AFF ? 2 : 1;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -558,7 +543,7 @@ inline SplitPlan split_plan(const QmmArgs& q) {
     // at most one workgroup per CU (a second round of a few workgroups, or
     // two per CU, measured slower), slices of whole wave-load steps, x slice
     // at most 32 KB of LDS
-    int S = QLIN_SPLIT_WGS / p.nsb;
+    int S = device_shape().cus / p.nsb;
     if (S < 1) S = 1;
     int64_t ks = (q.K + S - 1) / S;
     ks = (ks + rows_step - 1) / rows_step * rows_step;
@@ -595,6 +580,7 @@ hipError_t launch_split_fmt(const QmmArgs& q, float* part, const SplitPlan& p, h
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
+    a.xcds = 1;   // the K-split grid is laid out by (superblock, slice) itself
     constexpr int PER = 32 / BITS;
     constexpr int GW = G / PER;
     constexpr int V4 = GW < 4 ? GW : (BITS < 4 ? BITS : 4);

@@ -51,7 +51,8 @@ struct PrefillArgs {
     const uint32_t* offsets;  // [E+1] index-row offset of each expert
     const uint32_t* tiles;    // [E+1] row-tile prefix of each expert
     int E, B;
-    int xgm;                  // plain form: the 8 XCDs as an xgm x (8/xgm) grid of tile blocks (0: rows)
+    int xcds;                 // XCDs of the device
+    int xgm;                  // plain form: the XCDs as an xgm x (xcds/xgm) grid of tile blocks (0: rows)
     OutBias ob;               // dense-layer bias (plain form)
 };
 
@@ -131,57 +132,70 @@ __device__ __forceinline__ void load_bytes(__amdgpu_buffer_rsrc_t r, uint32_t vo
     }
 }
 
-// Dequantize CPC codes (natural k order) into CPC/2 packed bf16 pairs.
+// Dequantization of one chunk in small pieces, so that the pieces can sit
+// between single MFMAs: prepare (scale, bias and, for packed integer codes,
+// the codes split into bytes), then one packed bf16 pair per piece.
 // Affine: bf16(fmaf(s, q, z)), the dequantized value rounded once to the
 // MFMA input type. Microscaled: exact decode times the group scale.
-template <int MODE, int BITS, int WORDS>
-__device__ __forceinline__ void dequant_chunk(const Chunk<WORDS>& c, float s, float z,
-                                              uint32_t* out) {
-    constexpr int PER = 32 / BITS;
+template <int MODE, int BITS>
+struct DqPre {
+    static constexpr int N = MODE == AFFINE && BITS == 4 ? 2 : (MODE == AFFINE && BITS == 2 ? 4 : 1);
+};
+template <int MODE, int BITS, int NWO>
+struct DqState {
+    float s, z;
+    uint32_t pre[DqPre<MODE, BITS>::N];
+    uint32_t o[NWO];
+};
+
+// The codes of a chunk (WORDS dwords) split into bytes: 4-bit codes as the
+// low and high nibbles of each byte, 2-bit codes as four planes. The empty
+// asm keeps the masked words opaque, so each code is one byte convert
+// instead of a bit-field extract and a convert.
+template <int MODE, int BITS, int WORDS, int NWO>
+__device__ __forceinline__ void dq_prepare(DqState<MODE, BITS, NWO>& st, const uint32_t* w) {
+    if constexpr (MODE == AFFINE && BITS == 4) {
+        uint32_t lo = w[0] & 0x0F0F0F0Fu, hi = (w[0] >> 4) & 0x0F0F0F0Fu;
+        asm("" : "+v"(lo));
+        asm("" : "+v"(hi));
+        st.pre[0] = lo;
+        st.pre[1] = hi;
+    } else if constexpr (MODE == AFFINE && BITS == 2) {
 #pragma unroll
-    for (int wd = 0; wd < WORDS; ++wd) {
-        const uint32_t v = c.w[wd];
-        if constexpr (MODE == AFFINE) {
-            float f[PER];
-            if constexpr (BITS == 4) {
-                const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    f[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
-                    f[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
-                }
-            } else if constexpr (BITS == 8) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) f[b] = (float)((v >> (8 * b)) & 0xFFu);
-            } else {
-                const uint32_t b0 = v & 0x03030303u, b1 = (v >> 2) & 0x03030303u,
-                               b2 = (v >> 4) & 0x03030303u, b3 = (v >> 6) & 0x03030303u;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    f[4 * b] = (float)((b0 >> (8 * b)) & 0xFFu);
-                    f[4 * b + 1] = (float)((b1 >> (8 * b)) & 0xFFu);
-                    f[4 * b + 2] = (float)((b2 >> (8 * b)) & 0xFFu);
-                    f[4 * b + 3] = (float)((b3 >> (8 * b)) & 0xFFu);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < PER; e += 2)
-                out[wd * PER / 2 + e / 2] =
-                    pack_bf16(__builtin_fmaf(s, f[e], z), __builtin_fmaf(s, f[e + 1], z));
-        } else if constexpr (MODE == NVFP4) {
-            out[wd * 4 + 0] = e2m1_pair_times<0>(v, s);
-            out[wd * 4 + 1] = e2m1_pair_times<1>(v, s);
-            out[wd * 4 + 2] = e2m1_pair_times<2>(v, s);
-            out[wd * 4 + 3] = e2m1_pair_times<3>(v, s);
-        } else if constexpr (BITS == 4) {  // mxfp4: the E8M0 scale is a power of two
-            out[wd * 4 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0));
-            out[wd * 4 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1));
-            out[wd * 4 + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2));
-            out[wd * 4 + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3));
-        } else {  // mxfp8
-            out[wd * 2 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, false));
-            out[wd * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, true));
+        for (int j = 0; j < 4; ++j) {
+            uint32_t b = (w[0] >> (2 * j)) & 0x03030303u;
+            asm("" : "+v"(b));
+            st.pre[j] = b;
         }
+    }
+}
+
+template <int B>
+__device__ __forceinline__ float byte_f32(uint32_t v) {
+    return (float)((v >> (8 * B)) & 0xFFu);
+}
+
+// Packed bf16 pair Q (codes 2Q and 2Q + 1 of the chunk, natural k order).
+template <int MODE, int BITS, int WORDS, int NWO, int Q>
+__device__ __forceinline__ uint32_t dq_pair(const DqState<MODE, BITS, NWO>& st, const uint32_t* w) {
+    const float s = st.s, z = st.z;
+    if constexpr (MODE == AFFINE && BITS == 4) {
+        return pack_bf16(__builtin_fmaf(s, byte_f32<Q>(st.pre[0]), z),
+                         __builtin_fmaf(s, byte_f32<Q>(st.pre[1]), z));
+    } else if constexpr (MODE == AFFINE && BITS == 8) {
+        const uint32_t v = w[Q / 2];
+        return pack_bf16(__builtin_fmaf(s, byte_f32<(2 * Q) % 4>(v), z),
+                         __builtin_fmaf(s, byte_f32<(2 * Q) % 4 + 1>(v), z));
+    } else if constexpr (MODE == AFFINE) {   // 2-bit: code 4b + j is byte b of plane j
+        return pack_bf16(__builtin_fmaf(s, byte_f32<Q / 2>(st.pre[2 * (Q % 2)]), z),
+                         __builtin_fmaf(s, byte_f32<Q / 2>(st.pre[2 * (Q % 2) + 1]), z));
+    } else if constexpr (MODE == NVFP4) {
+        return e2m1_pair_times<Q>(w[0], s);
+    } else if constexpr (BITS == 4) {        // mxfp4: the E8M0 scale is a power of two
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[0], s, Q));
+    } else {                                  // mxfp8
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[Q / 2], s, (Q % 2) == 1));
     }
 }
 
@@ -235,23 +249,23 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         row_begin = (int)a.offsets[lo];
         row_count = ((int)a.offsets[lo + 1] - row_begin) * a.M;
     } else {
-        // Blocks are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8).
-        // With xgm > 0 the host has split the tile grid into xgm x (8/xgm)
-        // equal blocks, one per XCD, so an XCD's L2 fetches only its block's
-        // share of x and W (each XCD walking a row of tiles fetched all of
-        // W); otherwise each XCD walks a contiguous run of tiles along N.
-        int b = blockIdx.x;
-        const int nblk = gridDim.x;
+        // Blocks are dealt to the XCDs round-robin (XCD = blockIdx % xcds).
+        // With xgm > 0 the host has split the tile grid into xgm x
+        // (xcds/xgm) equal blocks, one per XCD, so an XCD's L2 fetches only
+        // its block's share of x and W (each XCD walking a row of tiles
+        // fetched all of W); otherwise each XCD walks a contiguous run of
+        // tiles along N.
+        const int b = blockIdx.x;
         if (a.xgm > 0) {
-            const int xgn = 8 / a.xgm, ntm = (a.M + BM - 1) / BM;
+            const int xgn = a.xcds / a.xgm, ntm = (a.M + BM - 1) / BM;
             const int mt = ntm / a.xgm, nt = ntn / xgn;      // tiles per XCD block
-            const int x = b & 7, j = b >> 3;
+            const int x = b % a.xcds, j = b / a.xcds;
             m0 = ((x / xgn) * mt + j / nt) * BM;
             n0 = ((x % xgn) * nt + j % nt) * BN;
         } else {
-            if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
-            m0 = (b / ntn) * BM;
-            n0 = (b % ntn) * BN;
+            const int bb = xcd_block(b, gridDim.x, a.xcds);
+            m0 = (bb / ntn) * BM;
+            n0 = (bb % ntn) * BN;
         }
     }
     // GEMM row rho of the tile's problem -> index row (gather) / x row / y row
@@ -360,47 +374,56 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
             if constexpr (MODE == AFFINE) load_bytes<NBB>(br, rowg[p], first * (int)SB, dz[p]);
         }
     };
-    // t: the step's place in its batch (compile time). The group of chunk
-    // (p, h) is (t * BK + k) / G within the batch, k its offset in the step;
+    // Dequantization of one step (step place T in its batch) as NITEM
+    // items: per chunk (p, h) of this thread, one item that decodes the
+    // scale and bias and splits the codes, NWO items of one packed bf16 pair
+    // each, and one item that writes the chunk to LDS. The group of chunk
+    // (p, h) is (T * BK + k) / G within the batch, k its offset in the step;
     // a step's scale bytes never straddle a dword, so the dword is known at
     // compile time and only the byte shift depends on the lane.
-    auto store_w = [&](unsigned char* base, const Chunk<RWORDS> (&wc)[CPT], const uint32_t (&sc)[CPT][BD],
-                       const uint32_t (&zc)[CPT][BD], auto tc) {
-        constexpr int T = decltype(tc)::value;
+    constexpr int NWO = CPC / 2;                  // packed bf16 pairs per chunk
+    constexpr int NCK = CPT * RCH;                // chunks per thread and step
+    constexpr int NITEM = NCK * (NWO + 2);
+    using DqSt = DqState<MODE, BITS, NWO>;
+    auto dq_item = [&](auto ic, DqSt (&st)[NCK], unsigned char* base, const Chunk<RWORDS> (&wc)[CPT],
+                       const uint32_t (&sc)[CPT][BD], const uint32_t (&zc)[CPT][BD], auto tc) {
+        constexpr int I = decltype(ic)::value, T = decltype(tc)::value;
+        constexpr int C = I / (NWO + 2), R = I % (NWO + 2);
+        constexpr int P = C / RCH, H = C % RCH;
         constexpr int DW = WHOLE ? (((T * BK) / G) * (int)SB) / 4 : 0;
         static_assert(DW < BD, "batch dword");
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            if (RCH == 1 && NCH % NTH != 0 && !cact[p]) continue;
-#pragma unroll
-            for (int h = 0; h < RCH; ++h) {
-                int sh = 0;
-                if constexpr (WHOLE && G >= BK) {
-                    sh = 8 * ((((T * BK) / G) * (int)SB) & 3);
-                } else if constexpr (WHOLE) {
-                    const int byte = ((T * BK + (ccv[p] + h) * CPC) / G) * (int)SB;
-                    sh = 8 * (byte - 4 * DW);
-                }
-                float sf, zf;
-                if constexpr (MODE == AFFINE) {
-                    sf = bf16_bits_to_f32((sc[p][DW] >> sh) & 0xFFFFu);
-                    zf = bf16_bits_to_f32((zc[p][DW] >> sh) & 0xFFFFu);
-                } else {
-                    const uint32_t byte = (sc[p][DW] >> sh) & 0xFFu;
-                    sf = MODE == NVFP4 ? e4m3_to_f32(byte) : e8m0_to_f32(byte);
-                    zf = 0.f;
-                }
-                Chunk<WORDS> ch;
-#pragma unroll
-                for (int q = 0; q < WORDS; ++q) ch.w[q] = wc[p].w[h * WORDS + q];
-                uint32_t o[CPC / 2];
-                dequant_chunk<MODE, BITS, WORDS>(ch, sf, zf, o);
-#pragma unroll
-                for (int q = 0; q < CPC / 8; ++q)
-                    *(u32x4*)(base + ldsoff[p] + h * CPC * 2 + q * 16) =
-                        u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        if constexpr (R == 0) {
+            int sh = 0;
+            if constexpr (WHOLE && G >= BK) {
+                sh = 8 * ((((T * BK) / G) * (int)SB) & 3);
+            } else if constexpr (WHOLE) {
+                const int byte = ((T * BK + (ccv[P] + H) * CPC) / G) * (int)SB;
+                sh = 8 * (byte - 4 * DW);
             }
+            if constexpr (MODE == AFFINE) {
+                st[C].s = bf16_bits_to_f32((sc[P][DW] >> sh) & 0xFFFFu);
+                st[C].z = bf16_bits_to_f32((zc[P][DW] >> sh) & 0xFFFFu);
+            } else {
+                const uint32_t byte = (sc[P][DW] >> sh) & 0xFFu;
+                st[C].s = MODE == NVFP4 ? e4m3_to_f32(byte) : e8m0_to_f32(byte);
+                st[C].z = 0.f;
+            }
+            dq_prepare<MODE, BITS, WORDS, NWO>(st[C], &wc[P].w[H * WORDS]);
+        } else if constexpr (R <= NWO) {
+            st[C].o[R - 1] = dq_pair<MODE, BITS, WORDS, NWO, R - 1>(st[C], &wc[P].w[H * WORDS]);
+        } else {
+            if (RCH == 1 && NCH % NTH != 0 && !cact[P]) return;
+#pragma unroll
+            for (int q = 0; q < CPC / 8; ++q)
+                *(u32x4*)(base + ldsoff[P] + H * CPC * 2 + q * 16) =
+                    u32x4{st[C].o[4 * q], st[C].o[4 * q + 1], st[C].o[4 * q + 2], st[C].o[4 * q + 3]};
         }
+    };
+    // the whole dequantization of one step, item after item
+    auto store_w = [&](unsigned char* base, const Chunk<RWORDS> (&wc)[CPT], const uint32_t (&sc)[CPT][BD],
+                       const uint32_t (&zc)[CPT][BD], auto tc) {
+        DqSt st[NCK];
+        unroll<0, NITEM>([&](auto ic) { dq_item(ic, st, base, wc, sc, zc, tc); });
     };
 
     // accumulators start at zero, or (OB: the dense layer's bias, a separate
@@ -489,33 +512,52 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* xt = smem + (kt % XST) * XSTAGE;
         const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
-        auto mma = [&](int kh0, int kh1) {
-#pragma unroll
-            for (int kh = kh0; kh < kh1; ++kh) {
-                u32x4 af[NT], bf[MT];
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    af[t] = *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
-#pragma unroll
-                for (int s2 = 0; s2 < MT; ++s2)
-                    bf[s2] = *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int s2 = 0; s2 < MT; ++s2) acc[t][s2] = mfma_bf16(af[t], bf[s2], acc[t][s2]);
-            }
+        auto rd_a = [&](int kh, int t) -> u32x4 {
+            return *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
         };
-        // step kt+1's weights (beyond the last step this fills an unused
-        // buffer), dequantized between the two halves of this step's MFMAs
-        mma(0, 1);
-        // step kt+1 is the next batch's first step when U is the last place
-        if constexpr (U + 1 < WPF)
-            store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wset[CUR], scur, zcur,
-                    std::integral_constant<int, U + 1>{});
-        else
-            store_w(wbuf + ((kt + 1) & 1) * WSTAGE, wset[CUR], snxt, znxt,
-                    std::integral_constant<int, 0>{});
-        mma(1, 2);
+        auto rd_b = [&](int kh, int s2) -> u32x4 {
+            return *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
+        };
+        // Issue order (scheduling barriers keep it): the first k half's
+        // fragments; then the step's 2 * NT * MT MFMAs one by one, after each
+        // its share of the next step's dequantization items (a few VALU
+        // instructions, which run while the MFMA does); the second half's
+        // weight fragment of row t is read once row t's first-half MFMAs are
+        // issued (same registers), its activation fragments during the
+        // first half's last rows.
+        constexpr int NS = 2 * NT * MT;
+        constexpr int SPAN = NS > 2 ? NS - 2 : 1;     // the last slots carry no items
+        constexpr int RB = NT >= 2 ? NT - 2 : 0;
+        u32x4 af[NT], bf0[MT], bf1[MT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) af[t] = rd_a(0, t);
+#pragma unroll
+        for (int s2 = 0; s2 < MT; ++s2) bf0[s2] = rd_b(0, s2);
+        __builtin_amdgcn_sched_barrier(0);
+        DqSt st[NCK];
+        constexpr int TN = U + 1 < WPF ? U + 1 : 0;  // step kt+1's place in its batch
+        unsigned char* const wnext = wbuf + ((kt + 1) & 1) * WSTAGE;
+        unroll<0, NS>([&](auto qc) {
+            constexpr int Q = decltype(qc)::value;
+            constexpr int KH = Q / (NT * MT), TT = (Q % (NT * MT)) / MT, SS = Q % MT;
+            if constexpr (KH == 0)
+                acc[TT][SS] = mfma_bf16(af[TT], bf0[SS], acc[TT][SS]);
+            else
+                acc[TT][SS] = mfma_bf16(af[TT], bf1[SS], acc[TT][SS]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (KH == 0 && SS == MT - 1) af[TT] = rd_a(1, TT);
+            if constexpr (KH == 0 && TT == RB) bf1[SS] = rd_b(1, SS);
+            // items I with I * SPAN / NITEM == Q
+            constexpr int ILO = (Q * NITEM + SPAN - 1) / SPAN, IHI = ((Q + 1) * NITEM + SPAN - 1) / SPAN;
+            unroll<(ILO < NITEM ? ILO : NITEM), (IHI < NITEM ? IHI : NITEM)>([&](auto ic) {
+                // step kt+1 is the next batch's first step when U is the last place
+                if constexpr (U + 1 < WPF)
+                    dq_item(ic, st, wnext, wset[CUR], scur, zcur, std::integral_constant<int, TN>{});
+                else
+                    dq_item(ic, st, wnext, wset[CUR], snxt, znxt, std::integral_constant<int, TN>{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
         constexpr int WAIT_IMM = wait_imm(U);
         __builtin_amdgcn_s_waitcnt(WAIT_IMM);
         asm volatile("s_barrier" ::: "memory");
@@ -557,12 +599,8 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     }
 }
 
-#ifndef QLIN_PREFILL_WPF
-#define QLIN_PREFILL_WPF 4
-#endif
-#ifndef QLIN_GATHER_WPF
-#define QLIN_GATHER_WPF 4
-#endif
+// code prefetch depth (steps): the plain and gather tiles alike
+constexpr int kPrefillWpf = 4;
 
 
 // Launch one kernel with `shm` bytes of dynamic LDS; the attribute that
@@ -590,7 +628,7 @@ hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     // bytes per row (16-byte batches of two sets push its registers over)
     constexpr int SBY = MODE == AFFINE ? 2 : 1;
     constexpr int B4 = (4 * BK / G > 0 ? 4 * BK / G : 1) * SBY;
-    constexpr int WPF = GATHER ? QLIN_GATHER_WPF : (B4 <= 8 ? QLIN_PREFILL_WPF : 2);
+    constexpr int WPF = GATHER ? kPrefillWpf : (B4 <= 8 ? kPrefillWpf : 2);
     const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
     static_assert(3 * BM * BK * 2 + 2 * BN * LROW <= 160 * 1024, "LDS budget");
     constexpr int NTH = WM * WN * 64;
@@ -606,17 +644,16 @@ hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
         t, grid, NTH, shm, st);
 }
 
-// XCD grid for the plain form: the 8 XCDs take an xgm x (8/xgm) grid of
-// equal tile blocks; xgm minimises what the XCDs fetch in all, xgm copies of
-// the weight plus 8/xgm copies of x (0: the tile grid does not split evenly).
-inline int xcd_grid_rows(int64_t ntm, int64_t ntn, double w_bytes, double x_bytes) {
-#ifdef QLIN_PREFILL_XCD_ROWS
-    return 0;
-#endif
+// XCD grid for the plain form: the xcds XCDs take an xgm x (xcds/xgm) grid
+// of equal tile blocks; xgm minimises what the XCDs fetch in all, xgm copies
+// of the weight plus xcds/xgm copies of x (0: the tile grid does not split
+// evenly).
+inline int xcd_grid_rows(int64_t ntm, int64_t ntn, double w_bytes, double x_bytes, int xcds) {
     int best = 0;
     double best_cost = 0;
-    for (int gm = 1; gm <= 8; gm <<= 1) {
-        const int gn = 8 / gm;
+    for (int gm = 1; gm <= xcds; ++gm) {
+        if (xcds % gm) continue;
+        const int gn = xcds / gm;
         if (ntm % gm || ntn % gn) continue;
         const double cost = gm * w_bytes + gn * x_bytes;
         if (best == 0 || cost < best_cost) {
@@ -632,7 +669,8 @@ hipError_t launch_plain(const PrefillArgs& t0, hipStream_t st) {
     PrefillArgs t = t0;
     const int64_t ntm = (t.M + BM - 1) / BM, ntn = (t.N + BN - 1) / BN;
     const double w_bytes = (double)t.N * t.K * BITS / 8.0, x_bytes = (double)t.M * t.K * 2.0;
-    t.xgm = xcd_grid_rows(ntm, ntn, w_bytes, x_bytes);
+    t.xcds = device_shape().xcds;
+    t.xgm = xcd_grid_rows(ntm, ntn, w_bytes, x_bytes, t.xcds);
     const int grid = (int)(ntm * ntn);
     if (t.ob.kind != OB_NONE) return launch_cfg<MODE, BITS, G, BM, BN, WM, WN, CPC0, false, true>(t, grid, st);
     return launch_cfg<MODE, BITS, G, BM, BN, WM, WN, CPC0, false>(t, grid, st);
@@ -702,20 +740,11 @@ hipError_t launch_gather_fmt(const QmmArgs& q, const uint32_t* perm, const uint3
     t.tiles = offsets + (q.E + 1);
     t.E = (int)q.E;
     t.B = (int)q.batch_x;
-#ifndef QLIN_GATHER_BN
-#define QLIN_GATHER_BN 192
-#endif
-    constexpr int BM = kPrefillGatherRows, BN = QLIN_GATHER_BN;
+    constexpr int BM = kPrefillGatherRows, BN = 192;
     // upper bound on row tiles: every expert may add one partial tile
     const int64_t mt = (q.R * q.M + BM - 1) / BM + q.E;
     const int grid = (int)(mt * ((q.N + BN - 1) / BN));
-#ifndef QLIN_GATHER_WAVES
-#define QLIN_GATHER_WAVES 0
-#endif
-    if constexpr (BM == 128 && QLIN_GATHER_WAVES == 1)
-        return launch_cfg<MODE, BITS, G, BM, BN, 4, 2, 8, true>(t, grid, st);
-    else
-        return launch_cfg<MODE, BITS, G, BM, BN, 2, 4, 8, true>(t, grid, st);
+    return launch_cfg<MODE, BITS, G, BM, BN, 2, 4, 8, true>(t, grid, st);
 }
 
 }  // namespace

@@ -60,6 +60,7 @@ struct Mx8Args {
     const uint8_t* ws;    // E8M0 [N, K/32]
     uint16_t* y;          // bf16 [M, N]
     int M, N, K;
+    int xcds;             // XCDs of the device (block renumbering)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -92,13 +93,11 @@ __global__ void __launch_bounds__(MX_THREADS) qqmm_mx8_kernel(Mx8Args a) {
     const uint32_t K = (uint32_t)a.K;
     const uint32_t KS = K / 32;                      // scale bytes per row
 
-    // tile of this workgroup: workgroups are dealt to the 8 XCDs round-robin;
+    // tile of this workgroup: workgroups are dealt to the XCDs round-robin;
     // renumber so each XCD walks a contiguous run of tiles, m fastest, and
     // the activation tiles sharing one weight tile meet in one L2
     const int ntm = (a.M + MX_BM - 1) / MX_BM;
-    int b = blockIdx.x;
-    const int nblk = gridDim.x;
-    if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
+    const int b = xcd_block(blockIdx.x, gridDim.x, a.xcds);
     const int m0 = (b % ntm) * MX_BM, n0 = (b / ntm) * MX_BN;
 
     const __amdgpu_buffer_rsrc_t xr = rsrc(a.xq, (uint32_t)a.M * K);
@@ -284,7 +283,7 @@ bool qqmm_mx8_supports(int64_t M, int64_t N, int64_t K, const void* wq, const vo
 hipError_t launch_qqmm_mx8(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                            uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
     if (!qqmm_mx8_supports(M, N, K, wq, ws)) return hipErrorNotSupported;
-    Mx8Args a{xq, xs, wq, ws, y, (int)M, (int)N, (int)K};
+    Mx8Args a{xq, xs, wq, ws, y, (int)M, (int)N, (int)K, device_shape().xcds};
     const int64_t tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
     const size_t shm = (size_t)2 * MX_XST * MX_STAGE + 2 * 4096;
     static std::atomic<bool> attr{false};

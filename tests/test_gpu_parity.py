@@ -278,6 +278,30 @@ def test_prefill_kernel_micro(M, mode, g, bits):
     run_qmm_case(M, 392, 512, bits, g, mode, "bf16", True, path="prefill", wid=92)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (17, 128, 256), (128, 128, 512), (300, 200, 512),
+                                   (257, 400, 768), (520, 385, 1024), (1024, 1024, 1024)])
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_prefill2_kernel_affine(M, N, K, g):
+    """Software-pipelined 4-bit kernel: 1-4 code blocks of 256 k (the ring
+    and block prefetch wrap), ragged M and N (N % 4 != 0 takes the scalar
+    stores), grids with and without the per-XCD tile blocks."""
+    run_qmm_case(M, N, K, 4, g, "affine", "bf16", True, path="prefill2", wid=95)
+
+
+def test_prefill2_kernel_refuses_other_shapes():
+    """K not a multiple of 256, or another bit width: the forced path fails
+    with a clear error instead of running."""
+    for (K, bits) in ((192, 4), (512, 8)):
+        w, _ = gpu_weight((64, K), 0.02, 96, "bf16")
+        qw = qm.quantize(w, 64, bits)
+        os.environ["QLIN_FORCE_PATH"] = "prefill2"
+        try:
+            with pytest.raises(RuntimeError, match="pipelined 4-bit prefill"):
+                qm.quantized_matmul(torch.ones(300, K, dtype=torch.bfloat16, device=DEV), qw)
+        finally:
+            os.environ.pop("QLIN_FORCE_PATH", None)
+
+
 @pytest.mark.parametrize("M", [1, 3, 4, 8])
 @pytest.mark.parametrize("bits,g", AFFINE_CASES)
 def test_nt_kernel_affine(M, bits, g):
@@ -623,6 +647,7 @@ DENSE_CASES = [
     (4, 1024, 512, 4, 64, "affine", "bf16", False, "decode"),     # [in, out] kernel
     (300, 400, 512, 4, 64, "affine", "bf16", True, "prefill"),    # many-row kernel, ragged
     (130, 256, 512, 8, 32, "mxfp8", "bf16", True, "prefill"),
+    (300, 402, 512, 4, 32, "affine", "bf16", True, "prefill2"),   # pipelined 4-bit kernel
     (300, 200, 512, 4, 64, "affine", "bf16", True, "tiled"),      # LDS-tiled kernel
     (5, 128, 256, 4, 64, "affine", "f32", True, "generic"),       # fp32 VALU kernels
     (5, 128, 256, 4, 64, "affine", "f16", False, "generic"),
