@@ -74,6 +74,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                              0x00020000);
 }
 
+// s_waitcnt immediate for vmcnt(vm) lgkmcnt(0). Fields: vmcnt [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8].
+constexpr int vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
+
 // f(integral_constant<int, U>) for U = B .. E-1, unrolled at compile time.
 template <int B, int E, class F>
 __device__ __forceinline__ void unroll(F&& f) {
@@ -301,7 +305,8 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     // filled by buffer->LDS loads. One wave instruction moves 8 rows (1 KB,
     // 16 bytes per lane, lane order). Row r keeps its 16-byte chunk c in slot
     // c ^ (r & 7), so the 16 rows an MFMA fragment reads at one k hit 8
-    // different slots (no LDS bank conflicts).
+    // different slots. (Also flipping the slot with bit 3 of the row, which
+    // spreads the 16 rows over 16 bank groups, measured 1-2 % slower.)
     const int wvu = __builtin_amdgcn_readfirstlane(wv);
     uint32_t xdoff[XDMA];
 #pragma unroll
@@ -460,120 +465,270 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
     uint32_t scur[CPT][BD], zcur[CPT][BD], snxt[CPT][BD], znxt[CPT][BD];
     unsigned char* const wbuf = smem + XST * XSTAGE;
 
-    // prologue: activations of steps 0 and 1 and codes of steps 0 .. WPF-1
-    // in flight, step by step, each step's activation loads first (the
-    // scheduling barriers keep that order: the waits below count on it);
-    // step 0's weights dequantized into buffer 0
-    constexpr int PRO = XLA > WPF ? XLA : WPF;
-    unroll<0, PRO>([&](auto u) {
-        constexpr int U = decltype(u)::value;
-        if constexpr (U < XLA) dma_x(U, U < nk ? U : nk - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (U < WPF) load_codes(wset[U], U < nk ? U : nk - 1);
-        if constexpr (U == 0) load_batch(scur, zcur, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    });
-    // waits for step 0's codes, issued after its activations
-    store_w(wbuf, wset[0], scur, zcur, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes done
-    asm volatile("s_barrier" ::: "memory");
-
-    // One step. Activation loads issued here land two steps later, code
-    // loads WPF steps later. vm operations complete in order; at the end of
-    // step kt the activations of step kt+1 (issued first in step kt-1, or in
-    // the prologue) must be in LDS, so the wait may leave outstanding only
-    // loads issued after them: step kt-1's code loads (and its batch of
-    // scales and biases when it opened a batch) and all of step kt's loads.
-    // With one step per batch (WPF = 1) only step kt's loads are counted
-    // (the prologue issues nothing after step 1's activations). The step ends
-    // with that wait, lgkmcnt(0) (this wave's LDS writes done) and a plain
-    // s_barrier: a fenced barrier would also wait for this step's loads.
     constexpr int WL = CPT * (RWORDS == 8 ? 2 : 1);            // code loads per step
     constexpr int BL = CPT * (MODE == AFFINE ? 2 : 1);         // batch loads (steps U = 0)
-    auto wait_imm = [](int U) constexpr {
-        int vm = XDMA + WL + (U == 0 ? BL : 0);                // this step
-        if (WPF > 1) vm += WL + (U == 1 ? BL : 0);             // step kt-1 after its activations
-        // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-        return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14);
+    auto rd_a = [&](const unsigned char* wt, int kh, int t) -> u32x4 {
+        return *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
     };
-    static_assert(XDMA + 2 * WL + 2 * BL < 64, "vmcnt range");
-    auto step = [&](int kt, auto uc) {
-        constexpr int U = decltype(uc)::value;          // kt % WPF
-        constexpr int CUR = (U + 1) % WPF;              // set of step kt+1 (dequantized now)
-        const int kx = kt + XLA < nk ? kt + XLA : nk - 1;
-        const int kw = kt + WPF < nk ? kt + WPF : nk - 1;
-        dma_x((kt + XLA) % XST, kx);
-        __builtin_amdgcn_sched_barrier(0);              // activations first (the wait counts on it)
-        load_codes(wset[U], kw);                        // set U held step kt, dequantized last step
-        if constexpr (U == 0) {
-            // the next batch (steps kt+WPF .. kt+2*WPF-1; past the end: the last batch)
-            load_batch(snxt, znxt, kt + WPF < nk ? kt + WPF : nk - WPF);
-        }
+    auto rd_b = [&](const unsigned char* xt, int kh, int s2) -> u32x4 {
+        return *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
+    };
+    constexpr int RB = NT >= 2 ? NT - 2 : 0;   // row during which the other half's activation fragments are read
+
+    if constexpr (WPF == 4) {
+        // ---- Pipelined form (batches of 4 steps). One barrier per step, in
+        // its middle, so that no wave starts MFMAs on fragments it has just
+        // asked for:
+        //   first half of step kt : MFMAs of k half 0; read k half 1's
+        //     fragments of step kt; dequantization items [NH, NITEM) of step
+        //     kt+1 (into W buffer (kt+1)&1)
+        //   barrier B_kt          : activations of step kt+1 in LDS, every
+        //     wave's dequantization of step kt+1 and reads of step kt's W
+        //     buffer and x stage complete (vmcnt as below, lgkmcnt(0))
+        //   second half           : DMA of step kt+3 (into step kt's x
+        //     stage), codes of step kt+4 (into step kt's code set), the next
+        //     batch of scales (U = 0); MFMAs of k half 1; read k half 0's
+        //     fragments of step kt+1; items [0, NH) of step kt+2 (into step
+        //     kt's W buffer, free since B_kt)
+        // Loads past the last step are clamped to it and their results are
+        // never used (reads of LDS the last steps overwrite are never used
+        // either).
+        constexpr int NH = NITEM / 2;
+        constexpr int SLOTS = NT * MT;
+        // vm operations complete in order. At B_kt the DMA of step kt+1
+        // (issued in the second half of step kt-2) must have landed; issued
+        // after it: the codes of that half, its batch when it opened one
+        // (U = 2), the next half's DMA and codes, and its batch (U = 1).
+        static_assert(XDMA + 2 * WL + BL < 64, "vmcnt range");
+        DqSt st[NCK];   // dequantization state carried from one half to the next
+        auto items = [&](auto lo, auto hi, auto q, auto span, DqSt (&s)[NCK], unsigned char* base,
+                         const Chunk<RWORDS> (&wc)[CPT], const uint32_t (&sc)[CPT][BD],
+                         const uint32_t (&zc)[CPT][BD], auto tc) {
+            // items [LO, HI) spread over SPAN slots; those of slot Q
+            constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
+            constexpr int Q = decltype(q)::value, SP = decltype(span)::value;
+            constexpr int N = HI - LO;
+            constexpr int A = LO + (Q * N + SP - 1) / SP, B = LO + ((Q + 1) * N + SP - 1) / SP;
+            unroll<(A < HI ? A : HI), (B < HI ? B : HI)>([&](auto ic) { dq_item(ic, s, base, wc, sc, zc, tc); });
+        };
+        constexpr int SPAN = SLOTS > 1 ? SLOTS - 1 : 1;   // the last slot of a half carries no items
+
+        // prologue. vm issue order: batch 0, codes 0, DMA 0, codes 1, DMA 1,
+        // codes 2, DMA 2, codes 3 -- after DMA 1 the loop's count for B_0
+        // (codes, DMA, codes); after DMA 2 that of B_1 with step 0's loads.
+        load_batch(scur, zcur, 0);
+        load_codes(wset[0], 0);
         __builtin_amdgcn_sched_barrier(0);
-        const unsigned char* xt = smem + (kt % XST) * XSTAGE;
-        const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
-        auto rd_a = [&](int kh, int t) -> u32x4 {
-            return *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
-        };
-        auto rd_b = [&](int kh, int s2) -> u32x4 {
-            return *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
-        };
-        // Issue order (scheduling barriers keep it): the first k half's
-        // fragments; then the step's 2 * NT * MT MFMAs one by one, after each
-        // its share of the next step's dequantization items (a few VALU
-        // instructions, which run while the MFMA does); the second half's
-        // weight fragment of row t is read once row t's first-half MFMAs are
-        // issued (same registers), its activation fragments during the
-        // first half's last rows.
-        constexpr int NS = 2 * NT * MT;
-        constexpr int SPAN = NS > 2 ? NS - 2 : 1;     // the last slots carry no items
-        constexpr int RB = NT >= 2 ? NT - 2 : 0;
+        dma_x(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(wset[1], 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_x(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(wset[2], 2);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_x(2, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(wset[3], 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // step 0's weights whole; the first half of step 1's items
+        store_w(wbuf, wset[0], scur, zcur, std::integral_constant<int, 0>{});
+        unroll<0, NH>([&](auto ic) {
+            dq_item(ic, st, wbuf + WSTAGE, wset[1], scur, zcur, std::integral_constant<int, 1>{});
+        });
+        // activations of step 0 in LDS (issued after them: codes 1, DMA 1,
+        // codes 2, DMA 2, codes 3), this wave's W writes done
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0(2 * XDMA + 3 * WL));
+        asm volatile("s_barrier" ::: "memory");
         u32x4 af[NT], bf0[MT], bf1[MT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) af[t] = rd_a(0, t);
+        for (int t = 0; t < NT; ++t) af[t] = rd_a(wbuf, 0, t);
 #pragma unroll
-        for (int s2 = 0; s2 < MT; ++s2) bf0[s2] = rd_b(0, s2);
+        for (int s2 = 0; s2 < MT; ++s2) bf0[s2] = rd_b(smem, 0, s2);
         __builtin_amdgcn_sched_barrier(0);
-        DqSt st[NCK];
-        constexpr int TN = U + 1 < WPF ? U + 1 : 0;  // step kt+1's place in its batch
-        unsigned char* const wnext = wbuf + ((kt + 1) & 1) * WSTAGE;
-        unroll<0, NS>([&](auto qc) {
-            constexpr int Q = decltype(qc)::value;
-            constexpr int KH = Q / (NT * MT), TT = (Q % (NT * MT)) / MT, SS = Q % MT;
-            if constexpr (KH == 0)
+
+        auto step = [&](int kt, auto uc) {
+            constexpr int U = decltype(uc)::value;       // kt % 4
+            const unsigned char* xt = smem + (kt % XST) * XSTAGE;
+            const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
+            const unsigned char* xn = smem + ((kt + 1) % XST) * XSTAGE;
+            const unsigned char* wn = wbuf + ((kt + 1) & 1) * WSTAGE;
+            unsigned char* const w1 = wbuf + ((kt + 1) & 1) * WSTAGE;   // step kt+1's W buffer
+            unsigned char* const w2 = wbuf + (kt & 1) * WSTAGE;         // step kt+2's W buffer
+            // ---- first half
+            unroll<0, SLOTS>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                constexpr int TT = Q / MT, SS = Q % MT;
                 acc[TT][SS] = mfma_bf16(af[TT], bf0[SS], acc[TT][SS]);
-            else
-                acc[TT][SS] = mfma_bf16(af[TT], bf1[SS], acc[TT][SS]);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (KH == 0 && SS == MT - 1) af[TT] = rd_a(1, TT);
-            if constexpr (KH == 0 && TT == RB) bf1[SS] = rd_b(1, SS);
-            // items I with I * SPAN / NITEM == Q
-            constexpr int ILO = (Q * NITEM + SPAN - 1) / SPAN, IHI = ((Q + 1) * NITEM + SPAN - 1) / SPAN;
-            unroll<(ILO < NITEM ? ILO : NITEM), (IHI < NITEM ? IHI : NITEM)>([&](auto ic) {
-                // step kt+1 is the next batch's first step when U is the last place
-                if constexpr (U + 1 < WPF)
-                    dq_item(ic, st, wnext, wset[CUR], scur, zcur, std::integral_constant<int, TN>{});
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SS == MT - 1) af[TT] = rd_a(wt, 1, TT);
+                if constexpr (TT == RB) bf1[SS] = rd_b(xt, 1, SS);
+                // step kt+1 = 4b + U + 1: batch b for U < 3, else b + 1
+                if constexpr (U < 3)
+                    items(std::integral_constant<int, NH>{}, std::integral_constant<int, NITEM>{}, qc,
+                          std::integral_constant<int, SPAN>{}, st, w1, wset[(U + 1) % 4], scur, zcur,
+                          std::integral_constant<int, (U + 1) % 4>{});
                 else
-                    dq_item(ic, st, wnext, wset[CUR], snxt, znxt, std::integral_constant<int, TN>{});
+                    items(std::integral_constant<int, NH>{}, std::integral_constant<int, NITEM>{}, qc,
+                          std::integral_constant<int, SPAN>{}, st, w1, wset[(U + 1) % 4], snxt, znxt,
+                          std::integral_constant<int, (U + 1) % 4>{});
+                __builtin_amdgcn_sched_barrier(0);
             });
+            __builtin_amdgcn_s_waitcnt(vm_lgkm0(XDMA + 2 * WL + ((U == 1 || U == 2) ? BL : 0)));
+            asm volatile("s_barrier" ::: "memory");
+            // ---- second half: loads first (the waits count on their order)
+            dma_x(kt % XST, kt + 3 < nk ? kt + 3 : nk - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            load_codes(wset[U], kt + 4 < nk ? kt + 4 : nk - 1);
+            if constexpr (U == 0) load_batch(snxt, znxt, kt + 4 < nk ? kt + 4 : nk - 4);
+            __builtin_amdgcn_sched_barrier(0);
+            unroll<0, SLOTS>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                constexpr int TT = Q / MT, SS = Q % MT;
+                acc[TT][SS] = mfma_bf16(af[TT], bf1[SS], acc[TT][SS]);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SS == MT - 1) af[TT] = rd_a(wn, 0, TT);
+                if constexpr (TT == RB) bf0[SS] = rd_b(xn, 0, SS);
+                // step kt+2 = 4b + U + 2: batch b for U < 2, else b + 1
+                if constexpr (U < 2)
+                    items(std::integral_constant<int, 0>{}, std::integral_constant<int, NH>{}, qc,
+                          std::integral_constant<int, SPAN>{}, st, w2, wset[(U + 2) % 4], scur, zcur,
+                          std::integral_constant<int, (U + 2) % 4>{});
+                else
+                    items(std::integral_constant<int, 0>{}, std::integral_constant<int, NH>{}, qc,
+                          std::integral_constant<int, SPAN>{}, st, w2, wset[(U + 2) % 4], snxt, znxt,
+                          std::integral_constant<int, (U + 2) % 4>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        // the host picks WPF dividing the step count: every unrolled step runs
+        for (int kt = 0; kt < nk; kt += 4) {
+            unroll<0, 4>([&](auto u) { step(kt + decltype(u)::value, u); });
+#pragma unroll
+            for (int p = 0; p < CPT; ++p)
+#pragma unroll
+                for (int d = 0; d < BD; ++d) {
+                    scur[p][d] = snxt[p][d];
+                    zcur[p][d] = znxt[p][d];
+                }
+        }
+    } else {
+        // prologue: activations of steps 0 and 1 and codes of steps 0 .. WPF-1
+        // in flight, step by step, each step's activation loads first (the
+        // scheduling barriers keep that order: the waits below count on it);
+        // step 0's weights dequantized into buffer 0
+        constexpr int PRO = XLA > WPF ? XLA : WPF;
+        unroll<0, PRO>([&](auto u) {
+            constexpr int U = decltype(u)::value;
+            if constexpr (U < XLA) dma_x(U, U < nk ? U : nk - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (U < WPF) load_codes(wset[U], U < nk ? U : nk - 1);
+            if constexpr (U == 0) load_batch(scur, zcur, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
-        constexpr int WAIT_IMM = wait_imm(U);
-        __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+        // waits for step 0's codes, issued after its activations
+        store_w(wbuf, wset[0], scur, zcur, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): this wave's LDS writes done
         asm volatile("s_barrier" ::: "memory");
-    };
-    // the host picks WPF dividing the step count, so every unrolled step runs
-    // (a conditional step would blur the compiler's load-count bookkeeping)
-    for (int kt = 0; kt < nk; kt += WPF) {
-        unroll<0, WPF>([&](auto u) { step(kt + decltype(u)::value, u); });
-#pragma unroll
-        for (int p = 0; p < CPT; ++p)
-#pragma unroll
-            for (int d = 0; d < BD; ++d) {
-                scur[p][d] = snxt[p][d];
-                zcur[p][d] = znxt[p][d];
+
+        // One step. Activation loads issued here land two steps later, code
+        // loads WPF steps later. vm operations complete in order; at the end of
+        // step kt the activations of step kt+1 (issued first in step kt-1, or in
+        // the prologue) must be in LDS, so the wait may leave outstanding only
+        // loads issued after them: step kt-1's code loads (and its batch of
+        // scales and biases when it opened a batch) and all of step kt's loads.
+        // With one step per batch (WPF = 1) only step kt's loads are counted
+        // (the prologue issues nothing after step 1's activations). The step ends
+        // with that wait, lgkmcnt(0) (this wave's LDS writes done) and a plain
+        // s_barrier: a fenced barrier would also wait for this step's loads.
+        auto wait_imm = [](int U) constexpr {
+            int vm = XDMA + WL + (U == 0 ? BL : 0);                // this step
+            if (WPF > 1) vm += WL + (U == 1 ? BL : 0);             // step kt-1 after its activations
+            // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+            return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14);
+        };
+        static_assert(XDMA + 2 * WL + 2 * BL < 64, "vmcnt range");
+        auto step = [&](int kt, auto uc) {
+            constexpr int U = decltype(uc)::value;          // kt % WPF
+            constexpr int CUR = (U + 1) % WPF;              // set of step kt+1 (dequantized now)
+            const int kx = kt + XLA < nk ? kt + XLA : nk - 1;
+            const int kw = kt + WPF < nk ? kt + WPF : nk - 1;
+            dma_x((kt + XLA) % XST, kx);
+            __builtin_amdgcn_sched_barrier(0);              // activations first (the wait counts on it)
+            load_codes(wset[U], kw);                        // set U held step kt, dequantized last step
+            if constexpr (U == 0) {
+                // the next batch (steps kt+WPF .. kt+2*WPF-1; past the end: the last batch)
+                load_batch(snxt, znxt, kt + WPF < nk ? kt + WPF : nk - WPF);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            const unsigned char* xt = smem + (kt % XST) * XSTAGE;
+            const unsigned char* wt = wbuf + (kt & 1) * WSTAGE;
+            auto rd_a = [&](int kh, int t) -> u32x4 {
+                return *(const u32x4*)(wt + (wn_ * NW + t * 16 + i) * LROW + (kh * 32 + 8 * j) * 2);
+            };
+            auto rd_b = [&](int kh, int s2) -> u32x4 {
+                return *(const u32x4*)(xt + xfrag0 + s2 * 2048 + (((kh * 4 + j) ^ (i & 7)) << 4));
+            };
+            // Issue order (scheduling barriers keep it): the first k half's
+            // fragments; then the step's 2 * NT * MT MFMAs one by one, after each
+            // its share of the next step's dequantization items (a few VALU
+            // instructions, which run while the MFMA does); the second half's
+            // weight fragment of row t is read once row t's first-half MFMAs are
+            // issued (same registers), its activation fragments during the
+            // first half's last rows.
+            constexpr int NS = 2 * NT * MT;
+            constexpr int SPAN = NS > 2 ? NS - 2 : 1;     // the last slots carry no items
+            constexpr int RB = NT >= 2 ? NT - 2 : 0;
+            u32x4 af[NT], bf0[MT], bf1[MT];
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) af[t] = rd_a(0, t);
+    #pragma unroll
+            for (int s2 = 0; s2 < MT; ++s2) bf0[s2] = rd_b(0, s2);
+            __builtin_amdgcn_sched_barrier(0);
+            DqSt st[NCK];
+            constexpr int TN = U + 1 < WPF ? U + 1 : 0;  // step kt+1's place in its batch
+            unsigned char* const wnext = wbuf + ((kt + 1) & 1) * WSTAGE;
+            unroll<0, NS>([&](auto qc) {
+                constexpr int Q = decltype(qc)::value;
+                constexpr int KH = Q / (NT * MT), TT = (Q % (NT * MT)) / MT, SS = Q % MT;
+                if constexpr (KH == 0)
+                    acc[TT][SS] = mfma_bf16(af[TT], bf0[SS], acc[TT][SS]);
+                else
+                    acc[TT][SS] = mfma_bf16(af[TT], bf1[SS], acc[TT][SS]);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (KH == 0 && SS == MT - 1) af[TT] = rd_a(1, TT);
+                if constexpr (KH == 0 && TT == RB) bf1[SS] = rd_b(1, SS);
+                // items I with I * SPAN / NITEM == Q
+                constexpr int ILO = (Q * NITEM + SPAN - 1) / SPAN, IHI = ((Q + 1) * NITEM + SPAN - 1) / SPAN;
+                unroll<(ILO < NITEM ? ILO : NITEM), (IHI < NITEM ? IHI : NITEM)>([&](auto ic) {
+                    // step kt+1 is the next batch's first step when U is the last place
+                    if constexpr (U + 1 < WPF)
+                        dq_item(ic, st, wnext, wset[CUR], scur, zcur, std::integral_constant<int, TN>{});
+                    else
+                        dq_item(ic, st, wnext, wset[CUR], snxt, znxt, std::integral_constant<int, TN>{});
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            constexpr int WAIT_IMM = wait_imm(U);
+            __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+            asm volatile("s_barrier" ::: "memory");
+        };
+        // the host picks WPF dividing the step count, so every unrolled step runs
+        // (a conditional step would blur the compiler's load-count bookkeeping)
+        for (int kt = 0; kt < nk; kt += WPF) {
+            unroll<0, WPF>([&](auto u) { step(kt + decltype(u)::value, u); });
+    #pragma unroll
+            for (int p = 0; p < CPT; ++p)
+    #pragma unroll
+                for (int d = 0; d < BD; ++d) {
+                    scur[p][d] = snxt[p][d];
+                    zcur[p][d] = znxt[p][d];
+                }
+        }
+
     }
+    // nothing of this workgroup may still be landing in LDS when it ends
+    __builtin_amdgcn_s_waitcnt(0);
 
     // ---- epilogue: lane holds D[n = 4j + r][m = i] of each (t, s) tile
 #pragma unroll
@@ -624,11 +779,17 @@ template <int MODE, int BITS, int G, int BM, int BN, int WM, int WN, int CPC0, b
 hipError_t launch_cfg(const PrefillArgs& t, int grid, hipStream_t st) {
     // a chunk holds at least one packed dword
     constexpr int CPC = CPC0 < 32 / BITS ? 32 / BITS : CPC0;
-    // the plain tile keeps 4-step batches of scales only where they fit 8
-    // bytes per row (16-byte batches of two sets push its registers over)
+    // The pipelined form (4-step batches) fits the registers of wave tiles
+    // of up to 16 MFMA tiles. On the 64 x 96 wave tile it needs 4-bit codes
+    // and batches of at most 8 bytes per row: 2-bit codes (four code planes
+    // per chunk), 8-bit codes (two dwords per chunk) or 16-byte batches (two
+    // sets) spill there (2-bit g64 ran 2.6x slower); those take the two-step
+    // form.
     constexpr int SBY = MODE == AFFINE ? 2 : 1;
     constexpr int B4 = (4 * BK / G > 0 ? 4 * BK / G : 1) * SBY;
-    constexpr int WPF = GATHER ? kPrefillWpf : (B4 <= 8 ? kPrefillWpf : 2);
+    constexpr int WTILES = (BM / WM / 16) * (BN / WN / 16);
+    constexpr bool PIPE = WTILES <= 16 || (B4 <= 8 && BITS == 4);
+    constexpr int WPF = GATHER ? kPrefillWpf : (PIPE ? kPrefillWpf : 2);
     const size_t shm = (size_t)3 * BM * BK * 2 + (size_t)2 * BN * LROW;
     static_assert(3 * BM * BK * 2 + 2 * BN * LROW <= 160 * 1024, "LDS budget");
     constexpr int NTH = WM * WN * 64;
