@@ -51,7 +51,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--only", choices=["all", "decode", "prefill", "headline"], default="all")
+    p.add_argument("--only", choices=["all", "decode", "prefill", "headline", "moe", "in_out", "micro",
+                                      "qqmm"], default="all",
+                   help="headline: the two headline workloads; moe, in_out, micro, qqmm: the "
+                        "decode headline plus that family alone (for profiling runs)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter scaling)")
     return p.parse_args()
@@ -370,6 +373,28 @@ def main():
             r = moe_case(False, T=T, wid=305)
             results.append(r)
             log(json.dumps(r))
+    if args.only == "in_out":   # [in,out] layout, M1 and M4
+        for M in (1, 4):
+            r = decode_case(M, 14336, 4096, 4, 64, transpose=False, wid=114)
+            results.append(r)
+            log(json.dumps(r))
+    if args.only == "micro":    # microscaled weights at 16 and 512 rows
+        for mode, g, bits in [("mxfp4", 32, 4), ("nvfp4", 16, 4), ("mxfp8", 32, 8)]:
+            r = decode_case(16, 8192, 8192, bits, g, mode=mode, wid=120)
+            results.append(r)
+            log(json.dumps(r))
+            r = prefill_case(512, 8192, 8192, bits, g, mode=mode, wid=203)
+            results.append(r)
+            log(json.dumps(r))
+    if args.only == "qqmm":
+        for mode in ("mxfp8", "nvfp4"):
+            r = qqmm_case(512, 8192, 8192, mode)
+            results.append(r)
+            log(json.dumps(r))
+    if args.only == "moe":
+        r = moe_case(False)
+        results.append(r)
+        log(json.dumps(r))
     if args.copy_probe:
         n = 256 * 2 ** 20
         a = torch.empty(n // 4, dtype=torch.int32, device=dev)

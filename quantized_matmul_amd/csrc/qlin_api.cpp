@@ -542,7 +542,7 @@ qlin_status qlin_gather_qmm(const void* x, qlin_dtype x_dtype, int64_t B, int64_
     else if (force == 2)
         return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this gather shape");
     else if ((force == 0 || force == 4) && qlin::qmm_prefill_supports(a))
-        tile_rows = qlin::kPrefillGatherRows;
+        tile_rows = qlin::prefill_gather_tile_rows(a.R * a.M, a.E);
     else if ((force == 0 || force == 3) && qlin::qmm_tiled_supports(a))
         tile_rows = qlin::kTiledGatherRows;
     if (tile_rows > 0) {

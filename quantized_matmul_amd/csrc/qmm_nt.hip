@@ -348,7 +348,7 @@ constexpr int SPLIT_NW = 8;                 // waves per workgroup
 
 template <int MODE, int BITS, int G, int MR, int VW>
 __global__ void __launch_bounds__(64 * SPLIT_NW) qmm_nt_split_kernel(NtArgs a, float* part, int ks,
-                                                                     int nsb) {
+                                                                     int nsb, int nreal) {
     constexpr int PER = 32 / BITS;
     constexpr int SBW = SPLIT_SBW, NWAVES = SPLIT_NW;
     static_assert((G / PER) % VW == 0, "a lane's words share one group");
@@ -363,7 +363,15 @@ __global__ void __launch_bounds__(64 * SPLIT_NW) qmm_nt_split_kernel(NtArgs a, f
     const int rr = lane / LPR, cl = lane % LPR;
     const int K = a.K, N = a.N, M = a.M;
     const int wcols = N / PER, gpr = N / G;
-    const int sb = blockIdx.x % nsb, sl = blockIdx.x / nsb;
+    // Workgroups are dealt to the XCDs round-robin. A 128-byte line of a
+    // row's scales (and biases) covers 64 groups, i.e. several neighbouring
+    // superblocks, so renumber the blocks XCD-major: each XCD walks a
+    // contiguous run of (slice, superblock) pairs and fetches each scale line
+    // once instead of once per XCD. The grid is padded to a multiple of the
+    // XCD count; the padding blocks leave at once.
+    const int L = xcd_block(blockIdx.x, gridDim.x, a.xcds);
+    if (L >= nreal) return;
+    const int sb = L % nsb, sl = L / nsb;
     const int k0 = sl * ks;
     const int kn = (K - k0) < ks ? (K - k0) : ks;      // rows of this slice (>= 1)
     const int c = sb * SBW + cl * VW;                  // first word column of the lane
@@ -560,7 +568,10 @@ hipError_t launch_split_kernel(const NtArgs& a, float* part, const SplitPlan& p,
     const size_t red = (size_t)SPLIT_NW * SPLIT_SBW * PER * 4;
     const size_t stage = (size_t)MR * p.ks * 2;
     const size_t shm = stage > red ? stage : red;
-    qmm_nt_split_kernel<MODE, BITS, G, MR, VW><<<p.nsb * p.S, 64 * SPLIT_NW, shm, st>>>(a, part, p.ks, p.nsb);
+    const int nreal = p.nsb * p.S;
+    const int xc = a.xcds > 1 ? a.xcds : 1;
+    const int grid = (nreal + xc - 1) / xc * xc;
+    qmm_nt_split_kernel<MODE, BITS, G, MR, VW><<<grid, 64 * SPLIT_NW, shm, st>>>(a, part, p.ks, p.nsb, nreal);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t quads = (int64_t)a.M * a.N / 4;
@@ -580,7 +591,7 @@ hipError_t launch_split_fmt(const QmmArgs& q, float* part, const SplitPlan& p, h
     a.M = (int)q.M;
     a.N = (int)q.N;
     a.K = (int)q.K;
-    a.xcds = 1;   // the K-split grid is laid out by (superblock, slice) itself
+    a.xcds = device_shape().xcds;
     constexpr int PER = 32 / BITS;
     constexpr int GW = G / PER;
     constexpr int V4 = GW < 4 ? GW : (BITS < 4 ? BITS : 4);

@@ -881,8 +881,9 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     }
 }
 
-// Expert-bucketed rows: BM = 64 rows of one expert (a typical expert's share
-// of a token batch), 192 weight rows, 32 x 48 per wave.
+// Expert-bucketed rows: BM = 64 or 128 rows of one expert (the same height
+// as the bucketing, prefill_gather_tile_rows), 192 weight rows, 32 x 48 or
+// 64 x 48 per wave.
 template <int MODE, int BITS, int G>
 hipError_t launch_gather_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets,
                              hipStream_t st) {
@@ -901,11 +902,13 @@ hipError_t launch_gather_fmt(const QmmArgs& q, const uint32_t* perm, const uint3
     t.tiles = offsets + (q.E + 1);
     t.E = (int)q.E;
     t.B = (int)q.batch_x;
-    constexpr int BM = kPrefillGatherRows, BN = 192;
+    constexpr int BN = 192;
+    const int BM = prefill_gather_tile_rows(q.R * q.M, q.E);
     // upper bound on row tiles: every expert may add one partial tile
     const int64_t mt = (q.R * q.M + BM - 1) / BM + q.E;
     const int grid = (int)(mt * ((q.N + BN - 1) / BN));
-    return launch_cfg<MODE, BITS, G, BM, BN, 2, 4, 8, true>(t, grid, st);
+    if (BM == 128) return launch_cfg<MODE, BITS, G, 128, BN, 2, 4, 8, true>(t, grid, st);
+    return launch_cfg<MODE, BITS, G, 64, BN, 2, 4, 8, true>(t, grid, st);
 }
 
 }  // namespace

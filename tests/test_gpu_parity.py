@@ -570,6 +570,28 @@ def test_gather_mfma_modes(mode, g, bits, path):
     run_gather_case(T, 3, 256, 200, E, rhs, lhs, bits=bits, g=g, mode=mode, path=path, wid=68)
 
 
+@pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8)] + MICRO_CASES)
+def test_gather_prefill_tall_tiles(mode, g, bits):
+    """48 or more rows per expert on average: the many-row kernel takes
+    128-row tiles of one expert (about 150 rows per expert here: one full
+    tile and a ragged one each), ragged N = 200."""
+    T, E, k = 100, 4, 2
+    rhs = synth.topk_distinct(T, E, k, 70)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+    run_gather_case(T, 3, 256, 200, E, rhs, lhs, bits=bits, g=g, mode=mode, path="prefill", wid=70)
+
+
+def test_gather_prefill_tall_tiles_skewed():
+    """128-row tiles with a hot expert (400 rows: four tiles), a small one
+    and empty ones, unsorted and sorted."""
+    rhs = np.array([5] * 400 + [0] * 30 + [2] * 130, np.uint32)
+    np.random.default_rng(4).shuffle(rhs)
+    run_gather_case(rhs.size, 1, 256, 96, 9, rhs, None, path="prefill", wid=71)
+    order = np.argsort(rhs, kind="stable")
+    run_gather_case(rhs.size, 1, 256, 96, 9, rhs[order], order.astype(np.uint32),
+                    sorted_indices=True, path="prefill", wid=71)
+
+
 @pytest.mark.parametrize("path", ["tiled", "prefill"])
 def test_gather_skewed_experts(path):
     """One hot expert with 150 rows (several row tiles), several empty ones."""
