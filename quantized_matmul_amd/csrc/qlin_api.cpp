@@ -40,6 +40,11 @@ DeviceShape device_shape() {
     return DeviceShape{c, x};
 }
 
+bool debug_lds_nan() {
+    const char* e = getenv("QLIN_DEBUG_LDS_NAN");
+    return e && e[0] == '1' && e[1] == 0;
+}
+
 // [in, out] layout with a caller's workspace (K split over workgroups)
 size_t qmm_nt_split_workspace_bytes(const QmmArgs& q);
 hipError_t launch_qmm_nt_split(const QmmArgs& q, void* workspace, hipStream_t st);

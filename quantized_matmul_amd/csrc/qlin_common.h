@@ -19,6 +19,12 @@ struct DeviceShape {
 };
 DeviceShape device_shape();
 
+// QLIN_DEBUG_LDS_NAN=1: the LDS-tiled kernels (many-row, pipelined 4-bit,
+// scaled fp8) fill their whole LDS with NaN bytes before each tile, so a
+// read of LDS that no load or store of the tile wrote -- a missing wait or
+// barrier, a wrong index -- turns the output into NaN. Read at each launch.
+bool debug_lds_nan();
+
 // Renumbers block b of nblk so that XCD x (= b % xcds) takes the contiguous
 // run [x * nblk / xcds, (x + 1) * nblk / xcds); a bijection when xcds divides
 // nblk, the identity otherwise.

@@ -52,6 +52,7 @@ struct PrefillArgs {
     const uint32_t* tiles;    // [E+1] row-tile prefix of each expert
     int E, B;
     int xcds;                 // XCDs of the device
+    int lds_nan;              // debug: fill LDS with NaN before the tile
     int xgm;                  // plain form: the XCDs as an xgm x (xcds/xgm) grid of tile blocks (0: rows)
     OutBias ob;               // dense-layer bias (plain form)
 };
@@ -271,6 +272,13 @@ __global__ void __launch_bounds__(WM * WN * 64) qmm_prefill_kernel(PrefillArgs a
             m0 = (bb / ntn) * BM;
             n0 = (bb % ntn) * BN;
         }
+    }
+    if (a.lds_nan) {   // debug: every LDS byte of the tile starts as NaN
+        constexpr int LDS_BYTES = XST * XSTAGE + 2 * WSTAGE;
+        static_assert(LDS_BYTES % 16 == 0, "16-byte fill");
+        for (int o = tid * 16; o < LDS_BYTES; o += NTH * 16)
+            *(u32x4*)(smem + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+        __syncthreads();
     }
     // GEMM row rho of the tile's problem -> index row (gather) / x row / y row
     auto x_row = [&](int rho) -> uint32_t {
@@ -871,6 +879,7 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
     t.N = (int)q.N;
     t.K = (int)q.K;
     t.ob = q.ob;
+    t.lds_nan = debug_lds_nan();
     int cfg = pick_cfg(q.M, q.N);
     if (const char* e = getenv("QLIN_PREFILL_TILE")) cfg = atoi(e) % 4;  // tests of each shape
     switch (cfg) {
@@ -902,6 +911,7 @@ hipError_t launch_gather_fmt(const QmmArgs& q, const uint32_t* perm, const uint3
     t.tiles = offsets + (q.E + 1);
     t.E = (int)q.E;
     t.B = (int)q.batch_x;
+    t.lds_nan = debug_lds_nan();
     constexpr int BN = 192;
     const int BM = prefill_gather_tile_rows(q.R * q.M, q.E);
     // upper bound on row tiles: every expert may add one partial tile

@@ -57,6 +57,7 @@ struct P2Args {
     uint16_t* y;             // bf16 [M, N]
     int M, N, K;
     int xcds;                // XCDs of the device
+    int lds_nan;             // debug: fill LDS with NaN before the tile
     int xgm;                 // the XCDs as an xgm x (xcds/xgm) grid of tile blocks (0: runs along N)
     OutBias ob;
 };
@@ -159,6 +160,11 @@ __global__ void __launch_bounds__(P2_THREADS, 2) qmm_prefill2_kernel(P2Args a) {
         }
     }
 
+    if (a.lds_nan) {   // debug: every LDS byte of the tile starts as NaN
+        for (int o = tid * 16; o < P2_XST * P2_XSTAGE; o += P2_THREADS * 16)
+            *(u32x4*)(smem + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+        __syncthreads();
+    }
     const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)a.M * K * 2u);
     const __amdgpu_buffer_rsrc_t wr = rsrc(a.wq, (uint32_t)a.N * (K / 2u));
     const uint32_t sbytes = (uint32_t)a.N * (K / G) * 2u;
@@ -392,6 +398,7 @@ hipError_t launch_p2_g(const QmmArgs& q, hipStream_t st) {
     t.N = (int)q.N;
     t.K = (int)q.K;
     t.ob = q.ob;
+    t.lds_nan = debug_lds_nan();
     const int64_t ntm = (q.M + P2_BM - 1) / P2_BM, ntn = (q.N + P2_BN - 1) / P2_BN;
     t.xcds = device_shape().xcds;
     t.xgm = p2_xcd_grid(ntm, ntn, (double)q.N * q.K / 2.0, (double)q.M * q.K * 2.0, t.xcds);

@@ -61,6 +61,7 @@ struct Mx8Args {
     uint16_t* y;          // bf16 [M, N]
     int M, N, K;
     int xcds;             // XCDs of the device (block renumbering)
+    int lds_nan;          // debug: fill LDS with NaN before the tile
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -98,6 +99,12 @@ __global__ void __launch_bounds__(MX_THREADS) qqmm_mx8_kernel(Mx8Args a) {
     // the activation tiles sharing one weight tile meet in one L2
     const int ntm = (a.M + MX_BM - 1) / MX_BM;
     const int b = xcd_block(blockIdx.x, gridDim.x, a.xcds);
+    if (a.lds_nan) {   // debug: every LDS byte of the tile starts as NaN
+        constexpr int LDS_BYTES = 2 * MX_XST * MX_STAGE + 2 * 4096;
+        for (int o = tid * 16; o < LDS_BYTES; o += MX_THREADS * 16)
+            *(u32x4*)(smem + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+        __syncthreads();
+    }
     const int m0 = (b % ntm) * MX_BM, n0 = (b / ntm) * MX_BN;
 
     const __amdgpu_buffer_rsrc_t xr = rsrc(a.xq, (uint32_t)a.M * K);
@@ -283,7 +290,7 @@ bool qqmm_mx8_supports(int64_t M, int64_t N, int64_t K, const void* wq, const vo
 hipError_t launch_qqmm_mx8(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws,
                            uint16_t* y, int64_t M, int64_t N, int64_t K, hipStream_t st) {
     if (!qqmm_mx8_supports(M, N, K, wq, ws)) return hipErrorNotSupported;
-    Mx8Args a{xq, xs, wq, ws, y, (int)M, (int)N, (int)K, device_shape().xcds};
+    Mx8Args a{xq, xs, wq, ws, y, (int)M, (int)N, (int)K, device_shape().xcds, debug_lds_nan() ? 1 : 0};
     const int64_t tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
     const size_t shm = (size_t)2 * MX_XST * MX_STAGE + 2 * 4096;
     static std::atomic<bool> attr{false};

@@ -795,3 +795,52 @@ def test_qqmm_scaled_mfma(case):
     err = normwise_rel_err(y, yref)
     print(f"qqmm scaled M{M} N{N} K{K}: err {err:.3e}", flush=True)
     assert err <= 4e-3
+
+
+# ---------------------------------------------------------------- debug mode
+
+@pytest.fixture
+def lds_nan_fill():
+    os.environ["QLIN_DEBUG_LDS_NAN"] = "1"
+    yield
+    os.environ.pop("QLIN_DEBUG_LDS_NAN", None)
+
+
+@pytest.mark.parametrize("case", [
+    (300, 200, 512, 4, 64, "affine", "prefill", None),    # pipelined form
+    (520, 385, 768, 8, 128, "affine", "prefill", "0"),    # 256 x 192 tile, two-step form
+    (300, 330, 512, 2, 32, "affine", "prefill", "0"),     # 2-bit, two-step form
+    (300, 330, 256, 2, 32, "affine", "prefill", None),    # 2-bit, 16-byte batches, pipelined
+    (130, 392, 512, 4, 32, "mxfp4", "prefill", None),
+    (600, 392, 512, 4, 16, "nvfp4", "prefill", None),
+    (300, 200, 512, 4, 64, "affine", "prefill2", None),   # register-dequantizing kernel
+], ids=lambda c: f"M{c[0]}N{c[1]}K{c[2]}{c[5]}b{c[3]}g{c[4]}-{c[6]}-t{c[7]}")
+def test_lds_nan_fill_qmm(case, lds_nan_fill):
+    """QLIN_DEBUG_LDS_NAN=1 fills each tile's LDS with NaN before the tile
+    starts; the outputs stay within the bar (a NaN fails it), so every LDS
+    byte an MFMA fragment reads was written by the tile first (ragged M, N)."""
+    M, N, K, bits, g, mode, path, tile = case
+    if tile is not None:
+        os.environ["QLIN_PREFILL_TILE"] = tile
+    try:
+        run_qmm_case(M, N, K, bits, g, mode, "bf16", True, path=path, wid=97)
+    finally:
+        os.environ.pop("QLIN_PREFILL_TILE", None)
+
+
+def test_lds_nan_fill_gather(lds_nan_fill):
+    """The gather form under the NaN fill: 128-row tiles (about 150 rows per
+    expert) and 64-row tiles (a few rows per expert)."""
+    T, E, k = 100, 4, 2
+    rhs = synth.topk_distinct(T, E, k, 98)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+    run_gather_case(T, 3, 256, 200, E, rhs, lhs, path="prefill", wid=98)
+    T, E, k = 40, 6, 2
+    rhs = synth.topk_distinct(T, E, k, 99)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), k).reshape(T, k)
+    run_gather_case(T, 3, 256, 200, E, rhs, lhs, bits=4, g=32, mode="mxfp4", path="prefill", wid=99)
+
+
+def test_lds_nan_fill_qqmm_scaled(lds_nan_fill):
+    """The scaled fp8 MFMA kernel under the NaN fill (ragged M and N)."""
+    test_qqmm_scaled_mfma((130, 200, 1024))
