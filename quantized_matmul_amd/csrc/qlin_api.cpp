@@ -232,8 +232,7 @@ qlin_status run_qmm(const qlin::QmmArgs& a, const uint32_t* perm, const uint32_t
         }
     }
     if (force == 2) return fail(QLIN_ERR_UNSUPPORTED, "decode kernel does not take this shape");
-    if (a.R == 0 && (force == 8 || (force == 0 && a.M >= qlin::kPrefill2MinRows)) &&
-        qlin::qmm_prefill2_supports(a)) {
+    if (a.R == 0 && force == 8 && qlin::qmm_prefill2_supports(a)) {
         note_path("prefill2");
         return device_status(qlin::launch_qmm_prefill2(a, st),
                              "quantized_matmul (pipelined 4-bit prefill kernel)");

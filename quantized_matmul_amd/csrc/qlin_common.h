@@ -183,9 +183,9 @@ hipError_t launch_qmm_prefill(const QmmArgs& a, const uint32_t* row_perm,
 bool qmm_prefill_supports(const QmmArgs& a);
 // Software-pipelined MFMA path for many rows of 4-bit affine weights
 // (transpose, bf16 x, K a multiple of 256): the weight is dequantized in
-// registers straight into the MFMA operand. Taken by default from
-// kPrefill2MinRows rows on.
-constexpr int64_t kPrefill2MinRows = int64_t(1) << 62;
+// registers straight into the MFMA operand. Slower than the LDS-tiled
+// many-row kernel on every measured shape, so it runs only when forced
+// (QLIN_FORCE_PATH=prefill2).
 hipError_t launch_qmm_prefill2(const QmmArgs& a, hipStream_t s);
 bool qmm_prefill2_supports(const QmmArgs& a);
 // VALU path for the [in, out] layout (transpose = false), M <= 8, bf16 x.
