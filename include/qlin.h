@@ -142,13 +142,18 @@ size_t qlin_quantized_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, in
  * workspace ("EMLX.Quantization" quantized_matmul, the same operation).
  * With at least qlin_quantized_matmul_workspace_bytes(...) bytes the
  * [in, out] layout at few rows splits K over workgroups: each stores fp32
- * partial sums of its slice of K in the workspace and a second kernel adds
- * the slices in a fixed order (results do not depend on scheduling). With
+ * partial sums of its slice of K in the workspace, and the workgroup that
+ * finishes a column block last adds its slices in a fixed order (results do
+ * not depend on scheduling) and writes y, all in one launch. With
  * workspace NULL, a smaller workspace or any other shape the call is
  * qlin_quantized_matmul's. The workspace is device memory the caller owns,
- * 16-byte aligned, overwritten; calls that share one workspace must not
- * overlap. Arguments and errors as for qlin_quantized_matmul, plus
- * QLIN_ERR_INVALID_ARGUMENT for a misaligned workspace.
+ * 16-byte aligned. Its first 4096 bytes hold completion counters: they must
+ * be zero before the workspace's first use (e.g. hipMemset once after
+ * allocating it) and every call leaves them zero; the rest is overwritten.
+ * Calls that share one workspace must not overlap, and a workspace that
+ * served another purpose must be zeroed again. Arguments and errors as for
+ * qlin_quantized_matmul, plus QLIN_ERR_INVALID_ARGUMENT for a misaligned
+ * workspace.
  */
 qlin_status qlin_quantized_matmul_ws(const void* x, qlin_dtype x_dtype, int64_t M, int64_t K,
                                      const uint32_t* wq, const void* scales, const void* biases,

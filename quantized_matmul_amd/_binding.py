@@ -184,6 +184,24 @@ def quantized_matmul_workspace_bytes(M: int, K: int, N: int, transpose: bool, gr
         M, K, N, int(transpose), group_size, bits, mode.encode()))
 
 
+# Zeroed workspaces for the K-split [in, out] calls, one per (device,
+# stream): the library keeps completion counters at the start of the
+# workspace, which must be zero before the first call and which every call
+# leaves zero, so a workspace is zeroed once (on its stream) and then reused
+# by the calls of that stream, which never overlap.
+_SPLIT_WS = {}
+
+
+def _split_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    stream = torch.cuda.current_stream(dev)
+    key = (dev.index, stream.cuda_stream)
+    ws = _SPLIT_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _SPLIT_WS[key] = ws
+    return ws
+
+
 def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
                      out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -192,8 +210,10 @@ def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
     W is 2-D: [N, K] packed along K when qw.transpose, else [K, N] packed
     along N ("Emily.Quantization.Layers", quantized_dense). Shapes that take
     a workspace (the [in, out] layout at few bf16 rows, where K is split over
-    workgroups) get one from torch's allocator unless `workspace` (a uint8
-    device tensor) is given; the call then goes to qlin_quantized_matmul_ws.
+    workgroups) use one zeroed workspace per device and stream, kept for
+    later calls, unless `workspace` (a uint8 device tensor whose first 4096
+    bytes are zero before its first use) is given; the call then goes to
+    qlin_quantized_matmul_ws.
     """
     lib = load_library()
     dev = _dev(x)
@@ -216,7 +236,8 @@ def quantized_matmul(x: torch.Tensor, qw: QuantizedWeight,
     elif not qw.transpose and x.dtype == torch.bfloat16 and 1 <= M <= 8:
         ws_bytes = quantized_matmul_workspace_bytes(M, K, N, False, qw.group_size, qw.bits, qw.mode)
         if ws_bytes:
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            workspace = _split_workspace(dev, ws_bytes)
+            ws_bytes = workspace.numel()
     if ws_bytes:
         rc = lib.qlin_quantized_matmul_ws(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(qw.value),
                                           _ptr(qw.scales), _ptr(qw.biases),

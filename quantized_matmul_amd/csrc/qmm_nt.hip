@@ -27,6 +27,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 struct NtArgs {
     const uint16_t* x;   // bf16 [M, K]
@@ -339,18 +340,30 @@ hipError_t launch_fmt(const QmmArgs& q, hipStream_t st) {
 // With a caller's workspace the rows of K are also split over workgroups:
 // workgroup (superblock, slice) covers SBW packed words of every weight row
 // (256 bytes: two whole cache lines, and one line of scales and of biases)
-// for the rows of its K slice, and stores its fp32 partial sums; a second
-// kernel adds the slices in order and writes y. Each workgroup then asks the
-// L2 for a few hundred rows instead of all K, four requests per 256 bytes
-// instead of three per 32.
+// for the rows of its K slice, and stores its fp32 partial sums. At one or
+// two activation rows the slice that finishes last for a superblock adds
+// the slices in order and writes y in the same launch (a separate summing
+// kernel cost about 2 us of a 16.8 us call); at three or four rows a second
+// kernel adds them. Each workgroup asks the L2 for a few hundred rows
+// instead of all K, four requests per 256 bytes instead of three per 32.
 constexpr int SPLIT_SBW = 64;   // packed words per superblock row
-constexpr int SPLIT_NW = 8;                 // waves per workgroup
+// The workspace starts with one completion counter per superblock (the
+// caller zeroes them once; every call leaves them zero), then the partial
+// sums [S][M][N] in fp32.
+constexpr size_t kSplitCounterBytes = 4096;
+// waves per workgroup (16 for one or two activation rows measured slower:
+// 15.0 against 14.5 us at one row)
+__host__ __device__ constexpr int split_nw(int) { return 8; }
+// the last slice adds the slices in the same kernel at one or two rows
+__host__ __device__ constexpr bool split_fuse(int mr) { return mr <= 2; }
 
 template <int MODE, int BITS, int G, int MR, int VW>
-__global__ void __launch_bounds__(64 * SPLIT_NW) qmm_nt_split_kernel(NtArgs a, float* part, int ks,
-                                                                     int nsb, int nreal) {
+__global__ void __launch_bounds__(64 * split_nw(MR)) qmm_nt_split_kernel(NtArgs a, float* part, uint32_t* cnt,
+                                                                     int ks, int S, int nsb,
+                                                                     int nreal) {
     constexpr int PER = 32 / BITS;
-    constexpr int SBW = SPLIT_SBW, NWAVES = SPLIT_NW;
+    constexpr int SBW = SPLIT_SBW, NWAVES = split_nw(MR);
+    constexpr bool FUSE = split_fuse(MR);
     static_assert((G / PER) % VW == 0, "a lane's words share one group");
     constexpr int LPR = SBW / VW;        // lanes per row
     constexpr int RPS = 64 / LPR;        // rows per wave load
@@ -458,17 +471,92 @@ __global__ void __launch_bounds__(64 * SPLIT_NW) qmm_nt_split_kernel(NtArgs a, f
                     acc[m][j * PER + e] = __builtin_fmaf(av[m], f[e], acc[m][j * PER + e]);
         }
     };
+    // 4-bit affine codes, two rows k0, k1 of a lane at a time: each column's
+    // pair of codes becomes the exact bf16 pair (128 + q0, 128 + q1) by byte
+    // permutes, and one v_dot2_f32_bf16 per column and activation row adds
+    // a0 * (128 + q0) + a1 * (128 + q1) with a = x * s rounded to bf16; the
+    // offset comes back out through the per-row term, which uses the same
+    // rounded a: zacc += x0 z0 + x1 z1 - 128 (a0 + a1).
+    auto consume2 = [&](int slot, int t) {
+        float av[2][MR];
+        uint32_t ab[MR];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kr = row_of(t + h);
+            const bool ok = active && kr < kn;
+            const int kk = ok ? kr : 0;
+            const float s = ok ? bf16_bits_to_f32(rs[slot + h] & 0xFFFFu) : 0.f;
+            const float z = ok ? bf16_bits_to_f32(rz[slot + h] & 0xFFFFu) : 0.f;
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float xv = bf16_bits_to_f32(xs[m * ks + kk]);
+                av[h][m] = xv * s;
+                zacc[m] = __builtin_fmaf(xv, z, zacc[m]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const bf16x2 p = {(__bf16)av[0][m], (__bf16)av[1][m]};
+            ab[m] = __builtin_bit_cast(uint32_t, p);
+            zacc[m] = __builtin_fmaf(-128.f, __uint_as_float(ab[m] << 16), zacc[m]);
+            zacc[m] = __builtin_fmaf(-128.f, __uint_as_float(ab[m] & 0xFFFF0000u), zacc[m]);
+        }
+        const uint32_t C = 0x43434343u;
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+            const uint32_t w0 = rw[slot][j], w1 = rw[slot + 1][j];
+            // nibble bytes: lo = codes 0, 2, 4, 6 and hi = codes 1, 3, 5, 7
+            const uint32_t lo[2] = {w0 & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu};
+            const uint32_t hi[2] = {(w0 >> 4) & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
+                const uint32_t l0 = par ? hi[0] : lo[0], l1 = par ? hi[1] : lo[1];
+                // bytes (row 0, row 1) of code bytes 0, 1 and of 2, 3
+                const uint32_t t01 = __builtin_amdgcn_perm(l1, l0, 0x05010400u);
+                const uint32_t t23 = __builtin_amdgcn_perm(l1, l0, 0x07030602u);
+                const uint32_t pr[4] = {__builtin_amdgcn_perm(C, t01, 0x04010400u),
+                                        __builtin_amdgcn_perm(C, t01, 0x04030402u),
+                                        __builtin_amdgcn_perm(C, t23, 0x04010400u),
+                                        __builtin_amdgcn_perm(C, t23, 0x04030402u)};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = j * PER + 2 * q + par;
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+                        acc[m][col] = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(bf16x2, ab[m]), __builtin_bit_cast(bf16x2, pr[q]),
+                            acc[m][col], false);
+                }
+            }
+        }
+    };
+    // (four rows keep the fp32 form: measured 23.2 against 23.9 us)
+    constexpr bool DOT2 = AFF && BITS == 4 && MR <= 2;
 #pragma unroll
     for (int r = 0; r < RING; ++r) fetch(r, r);
     for (int b = 0; b < T - RING; b += RING) {
+        if constexpr (DOT2) {
 #pragma unroll
-        for (int r = 0; r < RING; ++r) {
-            consume(r, b + r);
-            fetch(r, b + r + RING);
+            for (int r = 0; r < RING; r += 2) {
+                consume2(r, b + r);
+                fetch(r, b + r + RING);
+                fetch(r + 1, b + r + 1 + RING);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RING; ++r) {
+                consume(r, b + r);
+                fetch(r, b + r + RING);
+            }
         }
     }
+    if constexpr (DOT2) {
 #pragma unroll
-    for (int r = 0; r < RING; ++r) consume(r, T - RING + r);
+        for (int r = 0; r < RING; r += 2) consume2(r, T - RING + r);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) consume(r, T - RING + r);
+    }
 
     // sum the RPS row-lanes of each column, then the waves in LDS, and store
     // the slice's partial sums part[sl][m][n]
@@ -496,14 +584,71 @@ __global__ void __launch_bounds__(64 * SPLIT_NW) qmm_nt_split_kernel(NtArgs a, f
 #pragma unroll
             for (int w = 0; w < NWAVES; ++w) v += red[w * SBW * PER + o];
             const int n = sb * SBW * PER + o;
-            if (n < N) part[((size_t)sl * M + m) * N + n] = v;
+            if (n < N) {
+                if constexpr (FUSE)
+                    __hip_atomic_store(part + ((size_t)sl * M + m) * N + n, v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    part[((size_t)sl * M + m) * N + n] = v;
+            }
         }
         __syncthreads();
     }
+
+    // Completion: the slice that finishes last for this superblock adds the
+    // S slices' partial sums in slice order (the result does not depend on
+    // which slice that is), adds the dense bias, rounds once to bf16 and
+    // writes y, then puts the superblock's counter back to zero for the next
+    // call. The partial sums are written and read as agent-scope atomics,
+    // which are coherent across the XCDs' L2s without writing back or
+    // invalidating whole caches (an agent-scope fence per workgroup does
+    // that, and cost 45 us); every store has completed (the barrier waits
+    // for its vector memory counter) before one lane counts the slice in.
+    if constexpr (!FUSE) return;   // qmm_nt_split_reduce adds the slices
+    __shared__ int is_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(&cnt[sb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(S - 1);
+    __syncthreads();
+    if (!is_last) return;
+    // each thread takes one column at a time and has the loads of up to 16
+    // slices of every activation row in flight at once
+    const size_t stride = (size_t)M * N;
+    for (int o = tid; o < SBW * PER; o += 64 * NWAVES) {
+        const int n = sb * SBW * PER + o;
+        if (n >= N) break;
+        float v[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) v[m] = 0.f;
+        for (int s0 = 0; s0 < S; s0 += 16) {
+            float t[16][MR];
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    t[e][m] = (s0 + e < S && m < M)
+                                  ? __hip_atomic_load(part + (size_t)(s0 + e) * stride + (size_t)m * N + n,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    if (s0 + e < S) v[m] += t[e][m];
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            if (m < M) a.y[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(add_out_bias(a.ob, n, v[m]));
+    }
+    if (tid == 0) __hip_atomic_store(&cnt[sb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// y[m, n] = sum over the slices (in order) of part[s][m][n], plus the dense
-// bias, rounded once to bf16. A thread takes 4 adjacent outputs (N % 4 == 0)
+// Three or four activation rows: y[m, n] = sum over the slices (in order) of
+// part[s][m][n], plus the dense bias, rounded once to bf16, in a second
+// kernel (the in-kernel completion measured slower there: 25.3 against
+// 23.2 us at four rows). A thread takes 4 adjacent outputs (N % 4 == 0)
 // and has 8 slices' loads in flight at a time.
 __global__ void __launch_bounds__(256) qmm_nt_split_reduce(const float* part, int S, int M, int N,
                                                            uint16_t* y, OutBias ob) {
@@ -547,7 +692,7 @@ inline SplitPlan split_plan(const QmmArgs& q) {
     p.vw = vw;
     p.rps = 64 / (SPLIT_SBW / vw);
     p.nsb = (int)((wcols + SPLIT_SBW - 1) / SPLIT_SBW);
-    const int rows_step = p.rps * SPLIT_NW;
+    const int rows_step = p.rps * split_nw(mr);
     // at most one workgroup per CU (a second round of a few workgroups, or
     // two per CU, measured slower), slices of whole wave-load steps, x slice
     // at most 32 KB of LDS
@@ -563,15 +708,18 @@ inline SplitPlan split_plan(const QmmArgs& q) {
 }
 
 template <int MODE, int BITS, int G, int MR, int VW>
-hipError_t launch_split_kernel(const NtArgs& a, float* part, const SplitPlan& p, hipStream_t st) {
+hipError_t launch_split_kernel(const NtArgs& a, float* part, uint32_t* cnt, const SplitPlan& p,
+                               hipStream_t st) {
     constexpr int PER = 32 / BITS;
-    const size_t red = (size_t)SPLIT_NW * SPLIT_SBW * PER * 4;
+    const size_t red = (size_t)split_nw(MR) * SPLIT_SBW * PER * 4;
     const size_t stage = (size_t)MR * p.ks * 2;
     const size_t shm = stage > red ? stage : red;
     const int nreal = p.nsb * p.S;
     const int xc = a.xcds > 1 ? a.xcds : 1;
     const int grid = (nreal + xc - 1) / xc * xc;
-    qmm_nt_split_kernel<MODE, BITS, G, MR, VW><<<grid, 64 * SPLIT_NW, shm, st>>>(a, part, p.ks, p.nsb, nreal);
+    qmm_nt_split_kernel<MODE, BITS, G, MR, VW><<<grid, 64 * split_nw(MR), shm, st>>>(
+        a, part, cnt, p.ks, p.S, p.nsb, nreal);
+    if constexpr (split_fuse(MR)) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t quads = (int64_t)a.M * a.N / 4;
@@ -580,7 +728,8 @@ hipError_t launch_split_kernel(const NtArgs& a, float* part, const SplitPlan& p,
 }
 
 template <int MODE, int BITS, int G>
-hipError_t launch_split_fmt(const QmmArgs& q, float* part, const SplitPlan& p, hipStream_t st) {
+hipError_t launch_split_fmt(const QmmArgs& q, float* part, uint32_t* cnt, const SplitPlan& p,
+                            hipStream_t st) {
     NtArgs a;
     a.x = (const uint16_t*)q.x;
     a.wq = q.wq;
@@ -597,14 +746,14 @@ hipError_t launch_split_fmt(const QmmArgs& q, float* part, const SplitPlan& p, h
     constexpr int V4 = GW < 4 ? GW : (BITS < 4 ? BITS : 4);
     constexpr int V2 = GW < 2 ? GW : 2;
     if (nt_mr(a.M) == 1)
-        return p.vw == V4 ? launch_split_kernel<MODE, BITS, G, 1, V4>(a, part, p, st) : hipErrorInvalidValue;
+        return p.vw == V4 ? launch_split_kernel<MODE, BITS, G, 1, V4>(a, part, cnt, p, st) : hipErrorInvalidValue;
     if (nt_mr(a.M) == 2)
-        return p.vw == V4 ? launch_split_kernel<MODE, BITS, G, 2, V4>(a, part, p, st) : hipErrorInvalidValue;
+        return p.vw == V4 ? launch_split_kernel<MODE, BITS, G, 2, V4>(a, part, cnt, p, st) : hipErrorInvalidValue;
     if constexpr (BITS == 2) {
         return hipErrorNotSupported;   // 2-bit codes: one or two rows only (registers)
     } else {
         if (nt_mr(a.M) == 4)
-            return p.vw == V2 ? launch_split_kernel<MODE, BITS, G, 4, V2>(a, part, p, st) : hipErrorInvalidValue;
+            return p.vw == V2 ? launch_split_kernel<MODE, BITS, G, 4, V2>(a, part, cnt, p, st) : hipErrorInvalidValue;
         return hipErrorNotSupported;   // 5..8 rows: the one-pass kernel
     }
 }
@@ -649,37 +798,38 @@ size_t qmm_nt_split_workspace_bytes(const QmmArgs& q) {
     // 5..8 rows measured no faster split (34.4 against 33.8 us at M8, int4);
     // 2-bit codes' accumulators fit the registers at one or two rows only
     if (q.M > 4 || (q.bits == 2 && q.M > 2)) return 0;
-    if (q.N % 4 != 0) return 0;               // the sum kernel takes 4 outputs per thread
     const SplitPlan p = split_plan(q);
     // 16-byte words per lane need 16-byte aligned weight rows
     if (p.vw > 1 && ((uintptr_t)q.wq % (4 * p.vw)) != 0) return 0;
-    if (p.S < 2) return 0;
-    return (size_t)p.S * (size_t)q.M * (size_t)q.N * 4u;
+    if (p.S < 2 || p.nsb > kSplitCounterBytes / 4) return 0;
+    if (q.N % 4 != 0) return 0;               // the sum kernel takes 4 outputs per thread
+    return kSplitCounterBytes + (size_t)p.S * (size_t)q.M * (size_t)q.N * 4u;
 }
 
 hipError_t launch_qmm_nt_split(const QmmArgs& q, void* workspace, hipStream_t st) {
     if (qmm_nt_split_workspace_bytes(q) == 0) return hipErrorNotSupported;
     const SplitPlan p = split_plan(q);
-    float* part = (float*)workspace;
+    uint32_t* cnt = (uint32_t*)workspace;
+    float* part = (float*)((char*)workspace + kSplitCounterBytes);
     switch (q.mode) {
-    case MXFP4: return launch_split_fmt<MXFP4, 4, 32>(q, part, p, st);
-    case NVFP4: return launch_split_fmt<NVFP4, 4, 16>(q, part, p, st);
-    case MXFP8: return launch_split_fmt<MXFP8, 8, 32>(q, part, p, st);
+    case MXFP4: return launch_split_fmt<MXFP4, 4, 32>(q, part, cnt, p, st);
+    case NVFP4: return launch_split_fmt<NVFP4, 4, 16>(q, part, cnt, p, st);
+    case MXFP8: return launch_split_fmt<MXFP8, 8, 32>(q, part, cnt, p, st);
     default: break;
     }
     if (q.bits == 4) {
-        if (q.group_size == 32) return launch_split_fmt<AFFINE, 4, 32>(q, part, p, st);
-        if (q.group_size == 64) return launch_split_fmt<AFFINE, 4, 64>(q, part, p, st);
-        return launch_split_fmt<AFFINE, 4, 128>(q, part, p, st);
+        if (q.group_size == 32) return launch_split_fmt<AFFINE, 4, 32>(q, part, cnt, p, st);
+        if (q.group_size == 64) return launch_split_fmt<AFFINE, 4, 64>(q, part, cnt, p, st);
+        return launch_split_fmt<AFFINE, 4, 128>(q, part, cnt, p, st);
     }
     if (q.bits == 8) {
-        if (q.group_size == 32) return launch_split_fmt<AFFINE, 8, 32>(q, part, p, st);
-        if (q.group_size == 64) return launch_split_fmt<AFFINE, 8, 64>(q, part, p, st);
-        return launch_split_fmt<AFFINE, 8, 128>(q, part, p, st);
+        if (q.group_size == 32) return launch_split_fmt<AFFINE, 8, 32>(q, part, cnt, p, st);
+        if (q.group_size == 64) return launch_split_fmt<AFFINE, 8, 64>(q, part, cnt, p, st);
+        return launch_split_fmt<AFFINE, 8, 128>(q, part, cnt, p, st);
     }
-    if (q.group_size == 32) return launch_split_fmt<AFFINE, 2, 32>(q, part, p, st);
-    if (q.group_size == 64) return launch_split_fmt<AFFINE, 2, 64>(q, part, p, st);
-    return launch_split_fmt<AFFINE, 2, 128>(q, part, p, st);
+    if (q.group_size == 32) return launch_split_fmt<AFFINE, 2, 32>(q, part, cnt, p, st);
+    if (q.group_size == 64) return launch_split_fmt<AFFINE, 2, 64>(q, part, cnt, p, st);
+    return launch_split_fmt<AFFINE, 2, 128>(q, part, cnt, p, st);
 }
 
 }  // namespace qlin

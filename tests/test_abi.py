@@ -124,7 +124,8 @@ def test_quantized_matmul_ws_sizes_and_rejects(lib):
     the workspace entry point keeps qlin_quantized_matmul's checks."""
     nb = lib.qlin_quantized_matmul_workspace_bytes
     need = nb(1, 4096, 14336, 0, 64, 4, b"affine")
-    assert need > 0 and need % (14336 * 4) == 0          # whole fp32 partial rows
+    # 4096 bytes of completion counters, then whole fp32 partial rows
+    assert need > 4096 and (need - 4096) % (14336 * 4) == 0
     assert nb(4, 4096, 14336, 0, 64, 4, b"affine") > 0
     assert nb(8, 4096, 14336, 0, 64, 4, b"affine") == 0  # 5..8 rows: one-pass kernel
     assert nb(1, 4096, 14336, 1, 64, 4, b"affine") == 0  # [out, in] layout: none

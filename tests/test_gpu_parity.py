@@ -412,7 +412,7 @@ def test_nt_split_workspace_rules():
     x = xt.to(DEV)
     need = qm.quantized_matmul_workspace_bytes(2, K, N, False, 64, 4)
     assert need > 0
-    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)   # counters start at zero
     ys = [qm.quantized_matmul(x, qw, workspace=ws) for _ in range(3)]
     small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     y_small = qm.quantized_matmul(x, qw, workspace=small)
@@ -430,6 +430,39 @@ def test_nt_split_workspace_rules():
     tol = tolerance(torch.bfloat16, K)
     assert normwise_rel_err(ys[0], yref) <= tol
     assert normwise_rel_err(y_one, yref) <= tol
+    # every call leaves the completion counters at the start of the workspace zero
+    assert int(ws[:4096].count_nonzero()) == 0
+
+
+def test_nt_split_shared_workspace_shapes():
+    """One zeroed workspace serves K-split calls of different shapes, row
+    counts and formats in turn (the completion counters come back to zero
+    after each call); each result is bit-identical to the same call with a
+    fresh workspace and within the bar against the oracle."""
+    cases = [(1, 4096, 2048, 4, 64, 91), (3, 1536, 1024, 8, 32, 92), (2, 8192, 512, 4, 128, 93),
+             (1, 768, 4160, 2, 32, 94)]
+    prepared = []
+    need = 0
+    for M, N, K, bits, g, wid in cases:
+        w, wb = gpu_weight((K, N), 0.02, wid, "bf16")
+        xt, xb = synth.normal((M, K), 1.0, wid, synth.ACT, "bf16")
+        qw, ref = quantize_both(w, wb, "bf16", g, bits, "affine", False)
+        nb = qm.quantized_matmul_workspace_bytes(M, K, N, False, g, bits)
+        assert nb > 0
+        need = max(need, nb)
+        prepared.append((xt.to(DEV), xb, qw, ref, nb, M, K, g, bits))
+    shared = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        for x, xb, qw, (wq, sc, bi), nb, M, K, g, bits in prepared:
+            y = qm.quantized_matmul(x, qw, workspace=shared)
+            fresh = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+            y_fresh = qm.quantized_matmul(x, qw, workspace=fresh)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_fresh)
+            assert int(shared[:4096].count_nonzero()) == 0
+            yref = oracle.quantized_matmul(xb, "bf16", wq, sc, bi, False, g, bits, "affine",
+                                           scale_dtype="bf16")
+            assert normwise_rel_err(y, yref) <= tolerance(torch.bfloat16, K)
 
 
 @pytest.mark.parametrize("M", [9, 20, 128])
