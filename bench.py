@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", choices=["all", "decode", "prefill", "headline", "moe", "in_out", "micro",
-                                      "qqmm"], default="all",
+                                      "qqmm", "quant"], default="all",
                    help="headline: the two headline workloads; moe, in_out, micro, qqmm: the "
                         "decode headline plus that family alone (for profiling runs)")
     p.add_argument("--copy-probe", action="store_true",
@@ -355,8 +355,17 @@ def main():
         r = prefill_case(2048, 12288, 4096, 4, 64, wid=201, dense_bias=True)
         results.append(r)
         log(json.dumps(r))
-    if args.only == "all":
+    if args.only in ("all", "quant"):
         for (N, K, bits, g, mode) in [(14336, 4096, 4, 64, "affine"), (8192, 8192, 4, 32, "mxfp4")]:
+            for r in quant_case(N, K, bits, g, mode):
+                results.append(r)
+                log(json.dumps(r))
+    if args.only == "quant":   # and nvfp4, whose codes divide by the E4M3 scale
+        for r in quant_case(8192, 8192, 4, 16, "nvfp4"):
+            results.append(r)
+            log(json.dumps(r))
+    if args.only == "all":
+        for (N, K, bits, g, mode) in []:
             for r in quant_case(N, K, bits, g, mode):
                 results.append(r)
                 log(json.dumps(r))

@@ -152,6 +152,19 @@ __device__ __forceinline__ void load_chunk(const void* w, int64_t i, float (&v)[
     }
 }
 
+// The IEEE fp32 quotient d / s from r = 1/s correctly rounded in fp64:
+// (float)(d * r) rounds the fp64 product once more, to fp32. The product is
+// within 2^-52 (relative) of d / s, and a quotient of two 24-bit
+// significands that is not itself an fp32 value lies at least 2^-48 from
+// every fp32 rounding boundary in the normal range (a midpoint has 25
+// significant bits, and d - s * midpoint is a nonzero multiple of a unit
+// 2^-47 of d), so both roundings land on the same fp32 value. Quotients in
+// the subnormal range may differ in their last bit; every caller maps such
+// a value to code 0 (affine) or to a signed zero (E2M1), as it does the
+// exact quotient. One fp64 reciprocal per word replaces a division per
+// element, which bound the quantize kernels on VALU issue.
+__device__ __forceinline__ float div_by_recip(float d, double r) { return (float)((double)d * r); }
+
 // Min (MIN) or max of v over the LPG adjacent lanes of a group, LPG a power
 // of two <= 64. Each stage merges two neighbouring blocks of lanes with the
 // lower block's value as the first operand, so among equal values (+0 and
@@ -200,9 +213,10 @@ __device__ __forceinline__ void quantize_affine_word(const float (&v)[32 / BITS]
 
     uint32_t word = 0;
     if (s != 0.0f) {
+        const double r = 1.0 / (double)s;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-            float t = rintf(__fdiv_rn(v[e] - z, s));
+            float t = rintf(div_by_recip(v[e] - z, r));
             t = fminf(fmaxf(t, 0.0f), (float)n);
             word |= (uint32_t)t << (e * BITS);
         }
@@ -247,14 +261,16 @@ template <int MODE>
 struct MicroScale {
     uint32_t sbyte;
     float sc;   // nvfp4 element divisor
+    double rsc; // its fp64 reciprocal (0 when sc is 0)
     int e;      // mx shared exponent
 };
 template <int MODE>
 __device__ __forceinline__ MicroScale<MODE> micro_scale(float amax) {
-    MicroScale<MODE> m{0u, 0.0f, 0};
+    MicroScale<MODE> m{0u, 0.0f, 0.0, 0};
     if constexpr (MODE == NVFP4) {
         m.sbyte = e4m3_encode(__fdiv_rn(amax, 6.0f));
         m.sc = e4m3_to_f32(m.sbyte);
+        m.rsc = m.sc == 0.0f ? 0.0 : 1.0 / (double)m.sc;
     } else {
         constexpr int EMAX_ELEM = (MODE == MXFP8) ? 8 : 2;
         int e = (amax == 0.0f) ? -127 : floor_log2(amax) - EMAX_ELEM;
@@ -269,7 +285,7 @@ __device__ __forceinline__ MicroScale<MODE> micro_scale(float amax) {
 template <int MODE>
 __device__ __forceinline__ uint32_t micro_encode(float v, const MicroScale<MODE>& m) {
     if constexpr (MODE == NVFP4)
-        return (m.sc == 0.0f) ? ((__float_as_uint(v) >> 28) & 8u) : e2m1_encode(__fdiv_rn(v, m.sc));
+        return (m.sc == 0.0f) ? ((__float_as_uint(v) >> 28) & 8u) : e2m1_encode(div_by_recip(v, m.rsc));
     else if constexpr (MODE == MXFP8)
         return e4m3_encode(__builtin_ldexpf(v, -m.e));
     else

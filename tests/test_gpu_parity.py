@@ -93,6 +93,60 @@ def test_quantize_special_values_bit_exact():
                 assert np.array_equal(to_oracle(qw.biases), bi), (dtype, mode)
 
 
+def _nudge(v, k):
+    to = np.float32(np.inf if k > 0 else -np.inf)
+    v = np.float32(v)
+    for _ in range(abs(k)):
+        v = np.nextafter(v, to, dtype=np.float32)
+    return v
+
+
+@pytest.mark.parametrize("bits,a,k", [(8, 3, 0), (8, 63, 4), (4, 3, 6), (4, 11, 2), (2, 15, 9), (2, 25, 3)])
+def test_quantize_affine_quotient_edges(bits, a, k):
+    """The kernels' fp32 quotient d/s (an fp64 reciprocal product rounded
+    to fp32) against the oracle's IEEE division where it matters most:
+    groups with bias 0 and scale s = a*2^-k, elements on each half-step
+    (m + 1/2)*s and 1-2 ulps around it, so the codes turn on the exact
+    rounding of the quotient and on ties going to even."""
+    n = (1 << bits) - 1
+    g = 64
+    s = np.float32(a * 2.0 ** -k)
+    vals = []
+    for m in range(n):
+        tie = np.float32((m + 0.5) * s)
+        vals += [tie] + [_nudge(tie, d) for d in (-2, -1, 1, 2)]
+    per = g - 2
+    vals += [vals[-1]] * (-len(vals) % per)
+    rows = np.array(vals, np.float32).reshape(-1, per)
+    w = np.concatenate([np.zeros((len(rows), 1), np.float32),
+                        np.full((len(rows), 1), np.float32(n * s)), rows], axis=1)
+    wq, sc, bi = oracle.quantize(w, "f32", g, bits)
+    qw = qm.quantize(torch.from_numpy(w).to(DEV), g, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_oracle(qw.scales), sc)
+    assert np.array_equal(to_oracle(qw.value), wq)
+
+
+def test_quantize_quotient_random_scales():
+    """Random fp32 groups whose magnitudes span 2^-120 .. 2^120 (a different
+    scale exponent per group, normal and subnormal quotients alike): codes,
+    scales and biases bit-exact for affine 2/4/8-bit and nvfp4, whose
+    elements divide by the decoded E4M3 scale."""
+    r = np.random.default_rng(77)
+    rows, K = 512, 512
+    mag = np.float32(2.0) ** r.integers(-120, 121, size=(rows, K // 16)).astype(np.float32)
+    w = (r.standard_normal((rows, K)).astype(np.float32) * np.repeat(mag, 16, axis=1)).astype(np.float32)
+    wt = torch.from_numpy(w).to(DEV)
+    for mode, g, bits in [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8), ("nvfp4", 16, 4)]:
+        wq, sc, bi = oracle.quantize(w, "f32", g, bits, mode)
+        qw = qm.quantize(wt, g, bits, mode)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_oracle(qw.scales), sc), mode
+        assert np.array_equal(to_oracle(qw.value), wq), mode
+        if bi is not None:
+            assert np.array_equal(to_oracle(qw.biases), bi), mode
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode,g,bits", [("affine", 64, 4), ("affine", 32, 2), ("affine", 128, 8)] + MICRO_CASES)
 def test_quantize_dequantize_unaligned_pointers(dtype, mode, g, bits):
