@@ -151,7 +151,10 @@ size_t qlin_quantized_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N, in
  * be zero before the workspace's first use (e.g. hipMemset once after
  * allocating it) and every call leaves them zero; the rest is overwritten.
  * Calls that share one workspace must not overlap, and a workspace that
- * served another purpose must be zeroed again. Arguments and errors as for
+ * served another purpose must be zeroed again. A workspace whose counters
+ * hold a value at or past the number of K slices (memory that was never
+ * zeroed, typically) makes the call write NaN to the affected outputs, and
+ * every later call on it does the same, until it is zeroed. Arguments and errors as for
  * qlin_quantized_matmul, plus QLIN_ERR_INVALID_ARGUMENT for a misaligned
  * workspace.
  */

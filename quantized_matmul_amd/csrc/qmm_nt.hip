@@ -608,10 +608,24 @@ __global__ void __launch_bounds__(64 * split_nw(MR)) qmm_nt_split_kernel(NtArgs 
     __shared__ int is_last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0)
-        is_last = __hip_atomic_fetch_add(&cnt[sb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  (uint32_t)(S - 1);
+    // A count of S or more can only come from counters that were not zero
+    // when the call began (a workspace the caller did not zero): the slice
+    // takes its count back out and fills its columns of y with NaN, so such
+    // a call fails visibly, and so does every later call on that workspace.
+    if (tid == 0) {
+        const uint32_t old =
+            __hip_atomic_fetch_add(&cnt[sb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = old == (uint32_t)(S - 1) ? 1 : (old >= (uint32_t)S ? -1 : 0);
+        if (is_last < 0) __hip_atomic_fetch_sub(&cnt[sb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
+    if (is_last < 0) {
+        for (int o = tid; o < M * SBW * PER; o += 64 * NWAVES) {
+            const int m = o / (SBW * PER), n = sb * SBW * PER + o % (SBW * PER);
+            if (n < N) a.y[(size_t)m * N + n] = (uint16_t)0x7FC0u;   // bf16 quiet NaN
+        }
+        return;
+    }
     if (!is_last) return;
     // each thread takes one column at a time and has the loads of up to 16
     // slices of every activation row in flight at once

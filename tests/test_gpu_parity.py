@@ -488,6 +488,29 @@ def test_nt_split_workspace_rules():
     assert int(ws[:4096].count_nonzero()) == 0
 
 
+def test_nt_split_unzeroed_workspace_fails_visibly():
+    """A K-split workspace whose completion counters were never zeroed (all
+    bytes 0xFF here) makes every output of the call NaN, and of the next
+    call on it too; once zeroed, the same workspace gives the oracle's
+    result. The kernels run to completion either way."""
+    K, N = 2048, 4096
+    w, wb = gpu_weight((K, N), 0.02, 96, "bf16")
+    xt, xb = synth.normal((1, K), 1.0, 96, synth.ACT, "bf16")
+    qw, (wq, sc, bi) = quantize_both(w, wb, "bf16", 64, 4, "affine", False)
+    x = xt.to(DEV)
+    need = qm.quantized_matmul_workspace_bytes(1, K, N, False, 64, 4)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        y = qm.quantized_matmul(x, qw, workspace=ws)
+        torch.cuda.synchronize()
+        assert bool(torch.isnan(y.float()).all())
+    ws.zero_()
+    y = qm.quantized_matmul(x, qw, workspace=ws)
+    torch.cuda.synchronize()
+    yref = oracle.quantized_matmul(xb, "bf16", wq, sc, bi, False, 64, 4, "affine", scale_dtype="bf16")
+    assert normwise_rel_err(y, yref) <= tolerance(torch.bfloat16, K)
+
+
 def test_nt_split_shared_workspace_shapes():
     """One zeroed workspace serves K-split calls of different shapes, row
     counts and formats in turn (the completion counters come back to zero
