@@ -272,7 +272,7 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER, int CB>
 __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
-    static_assert(CB == 1 || CB == 2, "one or two column blocks per wave");
+    static_assert(CB == 1 || CB == 2 || CB == 4, "one, two or four column blocks per wave");
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
     static_assert(!GATHER || !DX, "the gather form stages x in LDS");
@@ -742,7 +742,7 @@ int pick_upw(int nunits, int M, bool dx) {
 template <int MODE, int BITS, int G, int UPW, bool DX, int CB = 1>
 hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, hipStream_t st) {
     constexpr int PF = UPW < kDecodePf ? UPW : kDecodePf;
-    if (CB == 2 && ks > 8) return hipErrorNotSupported;   // 512-thread kernels
+    if (CB >= 2 && ks > 8) return hipErrorNotSupported;   // 512-thread kernels
     const unsigned blocks = (unsigned)((a.N + a.cols * CB - 1) / (a.cols * CB));
     const dim3 grid(blocks, gather_tiles > 0 ? (unsigned)gather_tiles : 1u);
     const unsigned threads = 64u * (unsigned)ks;
@@ -758,7 +758,10 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, h
     };
     // group sums of x instead of the all-ones MFMA: affine, one row slot, M <= 4
     constexpr bool XSOK = Fmt<MODE, BITS, G>::AFF && Fmt<MODE, BITS, G>::S == 1 && !DX;
-    if constexpr (CB == 2) {
+    if constexpr (CB == 4) {
+        // staged x, 5..8 rows, plain form only
+        return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, false, 4>);
+    } else if constexpr (CB == 2) {
         if constexpr (DX) {
             // direct x, microscaled: rows past 4 in registers (MREG 4)
             return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, true, false, false, 2>);
@@ -863,8 +866,16 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
         const bool fits = DX || (int64_t)a.M * upw2 * F::U <= 4096;
         if (fits && nunits % upw2 == 0 && nunits / upw2 <= 8) {
             DecodeArgs a2 = a;
-            if (gather_tiles <= 0) a2.cols = decode_columns((a.N + 1) / 2, cus);
             const int ks2 = nunits / upw2;
+            if constexpr (!DX) {
+                // 5..8 staged rows: four column blocks per wave, so each
+                // workgroup's read of x from L2 serves four times the columns
+                if (gather_tiles <= 0 && a.M > 4 && upw2 == 4) {
+                    a2.cols = decode_columns((a.N + 3) / 4, cus);
+                    return launch_upw<MODE, BITS, G, 4, false, 4>(a2, ks2, mreg, 0, st);
+                }
+            }
+            if (gather_tiles <= 0) a2.cols = decode_columns((a.N + 1) / 2, cus);
             switch (upw2) {
             case 16: return launch_upw<MODE, BITS, G, 16, DX, 2>(a2, ks2, mreg, gather_tiles, st);
             case 8: return launch_upw<MODE, BITS, G, 8, DX, 2>(a2, ks2, mreg, gather_tiles, st);

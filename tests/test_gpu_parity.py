@@ -276,6 +276,15 @@ def test_decode_kernel_x_group_sums(M, K, bits, g):
     run_qmm_case(M, 40, K, bits, g, "affine", "bf16", True, path="decode", wid=24 + bits)
 
 
+@pytest.mark.parametrize("M", [5, 6, 7, 8])
+@pytest.mark.parametrize("N", [80, 1000])
+@pytest.mark.parametrize("bits,g", [(4, 64), (4, 128), (8, 32), (2, 32)])
+def test_decode_four_column_blocks(M, N, bits, g):
+    """5-8 staged activation rows: each wave covers four column blocks
+    (ragged rows, a ragged last block of columns, 2-bit g32's two row slots)."""
+    run_qmm_case(M, N, 2048, bits, g, "affine", "bf16", True, path="decode", wid=27 + bits)
+
+
 @pytest.mark.parametrize("M", [1, 5, 16])
 @pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
 def test_decode_kernel_micro(M, mode, g, bits):
