@@ -269,9 +269,16 @@ __device__ __forceinline__ void store_fragment_block(u32x4* dst, const u32x4* v)
 // blocks with the same x fragments, halving the x the workgroups re-read
 // from L2 (at M = 16 those reads, not the weight stream, set the time);
 // at most 8 waves per workgroup then, for the registers.
-template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER, int CB>
+template <int MODE, int BITS, int G, int UPW, int PF, int MREG, bool DX, bool XS, bool GATHER, int CB,
+          bool NS = false>
 __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(DecodeArgs a) {
     using F = Fmt<MODE, BITS, G>;
+    // NS (nvfp4, at most 8 rows): a K-step spans two 16-element groups, so
+    // the MFMA rows are split into two slots as for 2-bit g32 codes: codes
+    // go into the MFMA at unit scale (one convert per pair) and each step's
+    // two group sums take their E4M3 scales on the fp32 accumulator.
+    static_assert(!NS || (MODE == NVFP4 && !DX && !GATHER), "nvfp4 row slots: staged x, plain form");
+    constexpr int SL = NS ? 2 : F::S;   // row slots
     static_assert(CB == 1 || CB == 2 || CB == 4, "one, two or four column blocks per wave");
     static_assert(!DX || MODE != AFFINE, "direct x fragments need natural-order codes");
     static_assert(!XS || (F::AFF && F::S == 1 && !DX), "x group sums: affine codes, one row slot");
@@ -453,7 +460,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
     __builtin_amdgcn_sched_barrier(0);
     // ---- this lane's A row (zero row when it carries no real x row)
     int arow;
-    if constexpr (F::S == 2) arow = (i / 8 == j / 2 && (i & 7) < M) ? (i & 7) : M;
+    if constexpr (SL == 2) arow = (i / 8 == j / 2 && (i & 7) < M) ? (i & 7) : M;
     else arow = (i < M) ? i : M;
 
     // DX: A fragments of unit u from global memory. Fragment of global step
@@ -615,7 +622,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
                 u32x4 av;
                 if constexpr (DX) av = xcur[ls];
                 else av = *(const u32x4*)(abase + gs * 64);
-                const bool first = F::AFF && (ls % F::WS == 0);
+                const bool first = (F::AFF && (ls % F::WS == 0)) || NS;
                 if constexpr (F::AFF && !XS) dsum = mfma_bf16(av, ones, first ? zero4 : dsum);
 #pragma unroll
                 for (int b = 0; b < CB; ++b) {
@@ -627,8 +634,14 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
                         const int wd = (MODE == NVFP4) ? (uu * F::GPU + 2 * ls) / 4 : byte / 4;
                         sc = scale_byte_to_f32<MODE>((sraw[b][wd] >> (8 * (byte & 3))) & 0xFFu);
                     }
-                    const u32x4 bv = unpack<MODE, BITS, G>(wcur[b][r], t, sc);
+                    u32x4 bv;
+                    if constexpr (NS) bv = unpack<MXFP4, 4, 32>(wcur[b][r], t, 1.0f);   // E2M1 at unit scale
+                    else bv = unpack<MODE, BITS, G>(wcur[b][r], t, sc);
                     acc[b] = mfma_bf16(av, bv, first ? zero4 : acc[b]);
+                    if constexpr (NS) {
+#pragma unroll
+                        for (int rr = 0; rr < MREG; ++rr) ysum[b][rr] = __builtin_fmaf(sc, acc[b][rr], ysum[b][rr]);
+                    }
                 }
                 if constexpr (F::AFF) {
                     if (ls % F::WS == F::WS - 1) {
@@ -655,7 +668,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
             }
         }
     }
-    if constexpr (!F::AFF) {
+    if constexpr (!F::AFF && !NS) {
 #pragma unroll
         for (int b = 0; b < CB; ++b)
 #pragma unroll
@@ -675,7 +688,7 @@ __global__ void __launch_bounds__(CB == 1 ? 1024 : 512) qmm_decode_kernel(Decode
         if (n >= a.N || col >= a.cols) continue;
         float v = 0.f;
         for (int w = 0; w < KS; ++w) {
-            if constexpr (F::S == 2) {
+            if constexpr (SL == 2) {
                 v += red[((w * CB + b) * 16 + m) * 16 + col];
                 v += red[((w * CB + b) * 16 + 8 + m) * 16 + col];
             } else {
@@ -739,7 +752,7 @@ int pick_upw(int nunits, int M, bool dx) {
 
 // gather_tiles > 0: the gather form, blockIdx.y over that many row tiles
 // (an upper bound; tiles past the real count leave at once).
-template <int MODE, int BITS, int G, int UPW, bool DX, int CB = 1>
+template <int MODE, int BITS, int G, int UPW, bool DX, int CB = 1, bool NS = false>
 hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, hipStream_t st) {
     constexpr int PF = UPW < kDecodePf ? UPW : kDecodePf;
     if (CB >= 2 && ks > 8) return hipErrorNotSupported;   // 512-thread kernels
@@ -758,7 +771,21 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, h
     };
     // group sums of x instead of the all-ones MFMA: affine, one row slot, M <= 4
     constexpr bool XSOK = Fmt<MODE, BITS, G>::AFF && Fmt<MODE, BITS, G>::S == 1 && !DX;
-    if constexpr (CB == 4) {
+    if constexpr (NS) {   // nvfp4 row slots: staged x, plain form, at most 8 rows
+        if (gather_tiles > 0 || a.M > 8) return hipErrorNotSupported;
+        if constexpr (DX) {
+            return hipErrorNotSupported;
+        } else if constexpr (CB == 4) {
+            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, false, 4, true>);
+        } else if constexpr (CB == 2) {
+            if (mreg <= 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, false, false, false, 2, true>);
+            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, false, 2, true>);
+        } else {
+            if (mreg <= 1) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 1, false, false, false, 1, true>);
+            if (mreg == 2) return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 2, false, false, false, 1, true>);
+            return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, false, 1, true>);
+        }
+    } else if constexpr (CB == 4) {
         // staged x, 5..8 rows, plain form only
         return run(qmm_decode_kernel<MODE, BITS, G, UPW, PF, 4, false, false, false, 4>);
     } else if constexpr (CB == 2) {
@@ -793,7 +820,7 @@ hipError_t launch_upw(const DecodeArgs& a, int ks, int mreg, int gather_tiles, h
 
 // Plain form (perm == null) or gather form: rows bucketed by expert into
 // tiles of tile_rows GEMM rows (launch_bucket with the same tile height).
-template <int MODE, int BITS, int G, bool DX>
+template <int MODE, int BITS, int G, bool DX, bool NS = false>
 hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* offsets, int tile_rows,
                       hipStream_t st) {
     using F = Fmt<MODE, BITS, G>;
@@ -872,25 +899,25 @@ hipError_t launch_fmt(const QmmArgs& q, const uint32_t* perm, const uint32_t* of
                 // workgroup's read of x from L2 serves four times the columns
                 if (gather_tiles <= 0 && a.M > 4 && upw2 == 4) {
                     a2.cols = decode_columns((a.N + 3) / 4, cus);
-                    return launch_upw<MODE, BITS, G, 4, false, 4>(a2, ks2, mreg, 0, st);
+                    return launch_upw<MODE, BITS, G, 4, false, 4, NS>(a2, ks2, mreg, 0, st);
                 }
             }
             if (gather_tiles <= 0) a2.cols = decode_columns((a.N + 1) / 2, cus);
             switch (upw2) {
-            case 16: return launch_upw<MODE, BITS, G, 16, DX, 2>(a2, ks2, mreg, gather_tiles, st);
-            case 8: return launch_upw<MODE, BITS, G, 8, DX, 2>(a2, ks2, mreg, gather_tiles, st);
-            case 4: return launch_upw<MODE, BITS, G, 4, DX, 2>(a2, ks2, mreg, gather_tiles, st);
-            case 2: return launch_upw<MODE, BITS, G, 2, DX, 2>(a2, ks2, mreg, gather_tiles, st);
-            default: return launch_upw<MODE, BITS, G, 1, DX, 2>(a2, ks2, mreg, gather_tiles, st);
+            case 16: return launch_upw<MODE, BITS, G, 16, DX, 2, NS>(a2, ks2, mreg, gather_tiles, st);
+            case 8: return launch_upw<MODE, BITS, G, 8, DX, 2, NS>(a2, ks2, mreg, gather_tiles, st);
+            case 4: return launch_upw<MODE, BITS, G, 4, DX, 2, NS>(a2, ks2, mreg, gather_tiles, st);
+            case 2: return launch_upw<MODE, BITS, G, 2, DX, 2, NS>(a2, ks2, mreg, gather_tiles, st);
+            default: return launch_upw<MODE, BITS, G, 1, DX, 2, NS>(a2, ks2, mreg, gather_tiles, st);
             }
         }
     }
     switch (upw) {
-    case 16: return launch_upw<MODE, BITS, G, 16, DX>(a, ks, mreg, gather_tiles, st);
-    case 8: return launch_upw<MODE, BITS, G, 8, DX>(a, ks, mreg, gather_tiles, st);
-    case 4: return launch_upw<MODE, BITS, G, 4, DX>(a, ks, mreg, gather_tiles, st);
-    case 2: return launch_upw<MODE, BITS, G, 2, DX>(a, ks, mreg, gather_tiles, st);
-    default: return launch_upw<MODE, BITS, G, 1, DX>(a, ks, mreg, gather_tiles, st);
+    case 16: return launch_upw<MODE, BITS, G, 16, DX, 1, NS>(a, ks, mreg, gather_tiles, st);
+    case 8: return launch_upw<MODE, BITS, G, 8, DX, 1, NS>(a, ks, mreg, gather_tiles, st);
+    case 4: return launch_upw<MODE, BITS, G, 4, DX, 1, NS>(a, ks, mreg, gather_tiles, st);
+    case 2: return launch_upw<MODE, BITS, G, 2, DX, 1, NS>(a, ks, mreg, gather_tiles, st);
+    default: return launch_upw<MODE, BITS, G, 1, DX, 1, NS>(a, ks, mreg, gather_tiles, st);
     }
 }
 
@@ -934,7 +961,12 @@ hipError_t launch_mode(const QmmArgs& q, const uint32_t* perm, const uint32_t* o
                        hipStream_t st) {
     switch (q.mode) {
     case MXFP4: return launch_fmt<MXFP4, 4, 32, DX>(q, perm, offsets, tile_rows, st);
-    case NVFP4: return launch_fmt<NVFP4, 4, 16, DX>(q, perm, offsets, tile_rows, st);
+    case NVFP4:
+        // staged x, plain form, at most 8 rows: the row-slot kernel
+        if constexpr (!DX)
+            if (!perm && tile_rows == 0 && q.M <= 8)
+                return launch_fmt<NVFP4, 4, 16, false, true>(q, perm, offsets, tile_rows, st);
+        return launch_fmt<NVFP4, 4, 16, DX>(q, perm, offsets, tile_rows, st);
     case MXFP8: return launch_fmt<MXFP8, 8, 32, DX>(q, perm, offsets, tile_rows, st);
     default: break;
     }

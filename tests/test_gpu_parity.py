@@ -285,6 +285,15 @@ def test_decode_four_column_blocks(M, N, bits, g):
     run_qmm_case(M, N, 2048, bits, g, "affine", "bf16", True, path="decode", wid=27 + bits)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("N,K", [(48, 1024), (1000, 2048)])
+def test_decode_nvfp4_row_slots(M, N, K):
+    """nvfp4 at 1-8 rows: a K-step's two 16-element groups in two MFMA row
+    slots, codes at unit scale and the E4M3 scales on the accumulator
+    (ragged rows and columns, one-, two- and four-block forms)."""
+    run_qmm_case(M, N, K, 4, 16, "nvfp4", "bf16", True, path="decode", wid=33)
+
+
 @pytest.mark.parametrize("M", [1, 5, 16])
 @pytest.mark.parametrize("mode,g,bits", MICRO_CASES)
 def test_decode_kernel_micro(M, mode, g, bits):
